@@ -1,0 +1,407 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet hot path on one MI355X.
+
+Headline (the JSON line's ``value``): decode state throughput of the gated
+delta-rule recurrence for a batch of 256 independent sequences x 32 V-heads x
+S = 128 (fp32 state, 512 MiB): state bytes read + written per launch (1 GiB)
+divided by the time per launch. A step is one ``gdn_recurrence`` launch; the
+benchmark alternates between two independent state buffers so that no step
+finds its state in the 256 MB Infinity Cache.
+
+The same line carries the other workloads of the hot path ("legs"):
+  scan        1 sequence x 4096 tokens x 32 heads x S = 128: conv1d+SiLU over
+              the 4096 x 8192 activations, then the sequential scan; tokens/s
+  block       64 sequences x 48 layers of the fused bf16 decode layer (conv,
+              L2 norm + GQA repeat 16 -> 32, gate, sigmoid, recurrence, gated
+              RMSNorm), one launch per layer; ms per 48-layer step
+  decode_full the headline batch with its per-token glue launched too
+              (decay gate, sigmoid, L2 norm + GQA of q and k) before the
+              recurrence
+and the roofline of the dominant kernel (the decode recurrence) measured with
+HIP events on the stream it runs on, and the CPU oracle timed on this host.
+
+Inputs are seeded synthetic draws (numpy PCG64) with the workloads' shapes
+and distributions, uploaded before timing; the per-token glue of the
+recurrence inputs (q/k normalisation, gate, beta) runs on the GPU through the
+library before the timed region.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs decode,scan,block]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN decode state GB/s (% HBM peak) @32h S=128; scan tokens/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor specification
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, vendor specification
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--legs", default="decode,scan,block,decode_full")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+
+class Timer:
+    """Wall clock bracketed by device synchronisation, plus HIP events on the
+    current stream (the stream every library call here is enqueued on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def __enter__(self):
+        t = self.torch
+        t.cuda.synchronize()
+        self.ev0 = t.cuda.Event(enable_timing=True)
+        self.ev1 = t.cuda.Event(enable_timing=True)
+        self.w0 = time.perf_counter()
+        self.ev0.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.ev1.record()
+        self.torch.cuda.synchronize()
+        self.wall_ms = (time.perf_counter() - self.w0) * 1e3
+        self.event_ms = self.ev0.elapsed_time(self.ev1)
+        return False
+
+
+def parallel(fn, items, workers=16):
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(fn, items))
+
+
+def host_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        n = min(n, int(env))
+    return max(1, n)
+
+
+# ---------------------------------------------------------------------------
+# legs
+# ---------------------------------------------------------------------------
+
+def decode_inputs(torch, gdn, inputs):
+    w = inputs.WORKLOADS[2]
+    d = inputs.draw(w)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    N, H, HK, S = w.n_seqs, w.n_v_heads, w.n_k_heads, w.state_size
+    raw = {k: dev(d[k][:, 0]) for k in ("q_raw", "k_raw", "v", "a", "b")}
+    par = {k: dev(d[k]) for k in ("A_log", "dt_bias")}
+    q = torch.empty((N, H, S), device="cuda")
+    k = torch.empty((N, H, S), device="cuda")
+    g = torch.empty((N, H), device="cuda")
+    beta = torch.empty((N, H), device="cuda")
+
+    def glue():
+        gdn.gdn_l2norm_gqa(raw["q_raw"], q, w.l2_eps)
+        gdn.gdn_l2norm_gqa(raw["k_raw"], k, w.l2_eps)
+        gdn.gdn_decay_gate(raw["a"], par["dt_bias"], par["A_log"], g)
+        gdn.gdn_sigmoid(raw["b"], beta)
+
+    glue()
+    st0 = dev(d["state"])
+    states = [st0, st0.clone()]
+    y = torch.empty((N, H, S), device="cuda")
+    torch.cuda.synchronize()
+    return w, d, dict(q=q, k=k, v=raw["v"], g=g, beta=beta, y=y, states=states, glue=glue)
+
+
+def decode_bytes(w) -> dict:
+    N, H, S = w.n_seqs, w.n_v_heads, w.state_size
+    state = 2 * N * H * S * S * 4
+    vecs = 4 * N * H * S * 4          # q, k, v read; y written
+    scal = 2 * N * H * 4              # g, beta
+    return {"state": state, "total": state + vecs + scal}
+
+
+def run_decode(torch, gdn, inputs, steps, warmup, with_glue=False):
+    w, d, t = decode_inputs(torch, gdn, inputs)
+
+    def step(i):
+        if with_glue:
+            t["glue"]()
+        gdn.gdn_recurrence(t["states"][i % 2], t["q"], t["k"], t["v"], t["g"], t["beta"],
+                           t["y"], w.scale)
+
+    for i in range(warmup):
+        step(i)
+    with Timer(torch) as tm:
+        for i in range(steps):
+            step(i)
+    b = decode_bytes(w)
+    ms_wall = tm.wall_ms / steps
+    ms_ev = tm.event_ms / steps
+    res = {
+        "workload": "batched decode: 256 sequences x 32 V-heads x S=128, fp32 state 512 MiB",
+        "ms_per_step": ms_wall,
+        "kernel_ms_events": ms_ev,
+        "state_GBps": b["state"] / (ms_wall * 1e-3) / 1e9,
+        "total_GBps": b["total"] / (ms_wall * 1e-3) / 1e9,
+        "algorithmic_bytes_per_launch": b["total"],
+        "state_bytes_per_launch": b["state"],
+    }
+    return w, d, res
+
+
+def run_scan(torch, gdn, inputs, steps, warmup):
+    w = inputs.WORKLOADS[3]
+    d = inputs.draw(w)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    N, T, H, HK, S, C = w.n_seqs, w.n_tokens, w.n_v_heads, w.n_k_heads, w.state_size, w.conv_dim
+    q = torch.empty((N, T, H, S), device="cuda")
+    k = torch.empty((N, T, H, S), device="cuda")
+    g = torch.empty((N, T, H), device="cuda")
+    beta = torch.empty((N, T, H), device="cuda")
+    gdn.gdn_l2norm_gqa(dev(d["q_raw"]), q, w.l2_eps)
+    gdn.gdn_l2norm_gqa(dev(d["k_raw"]), k, w.l2_eps)
+    gdn.gdn_decay_gate(dev(d["a"]), dev(d["dt_bias"]), dev(d["A_log"]), g)
+    gdn.gdn_sigmoid(dev(d["b"]), beta)
+    v = dev(d["v"])
+    st = dev(d["state"])
+    y = torch.empty((N, T, H, S), device="cuda")
+    x = dev(d["x"])
+    cw = dev(d["conv_w"])
+    cs = dev(d["conv_state"])
+    co = torch.empty_like(x)
+    torch.cuda.synchronize()
+
+    def conv():
+        gdn.gdn_conv1d_silu_seq(x, cw, cs, co)
+
+    def scan():
+        gdn.gdn_recurrence_seq(st, q, k, v, g, beta, y, w.scale)
+
+    for _ in range(warmup):
+        conv()
+        scan()
+    with Timer(torch) as t_all:
+        for _ in range(steps):
+            conv()
+            scan()
+    with Timer(torch) as t_conv:
+        for _ in range(steps):
+            conv()
+    with Timer(torch) as t_scan:
+        for _ in range(steps):
+            scan()
+    ms = t_all.wall_ms / steps
+    scan_ms = t_scan.event_ms / steps
+    conv_ms = t_conv.event_ms / steps
+    flops = 7.0 * N * T * H * S * S        # 1 mul + 3 fma per state element and token
+    conv_bytes = 2 * N * T * C * 4 + C * w.conv_kernel * 4 + 2 * N * C * (w.conv_kernel - 1) * 4
+    scan_bytes = (4 * N * T * H * S + 2 * N * T * H) * 4 + 2 * N * H * S * S * 4
+    return {
+        "workload": "sequential scan: 1 sequence x 4096 tokens x 32 heads x S=128 fp32, "
+                    "preceded by conv1d+SiLU over 4096 x 8192 (K=4)",
+        "ms_per_step": ms,
+        "tokens_per_s": N * T / (ms * 1e-3),
+        "scan_kernel_ms": scan_ms,
+        "scan_tokens_per_s": N * T / (scan_ms * 1e-3),
+        "scan_TFLOPs": flops / (scan_ms * 1e-3) / 1e12,
+        "scan_frac_fp32_vector_peak": flops / (scan_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+        "scan_algorithmic_bytes": scan_bytes,
+        "conv_kernel_ms": conv_ms,
+        "conv_GBps": conv_bytes / (conv_ms * 1e-3) / 1e9,
+        "conv_frac_hbm_peak": conv_bytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+    }
+
+
+def block_layer_bytes(N, H, HK, S, K) -> int:
+    C = 2 * HK * S + H * S
+    return (2 * N * H * S * S * 4            # state read + write
+            + 2 * N * C * (K - 1) * 4        # conv history read + write
+            + N * C * 2 + N * H * S * 2      # qkv, z (bf16)
+            + N * H * S * 4                  # out
+            + C * K * 4 + 2 * N * H * 4 + 2 * H * 4 + S * 4)
+
+
+def run_block(torch, gdn, inputs, steps, warmup):
+    w = inputs.WORKLOADS[4]
+    N, H, HK, S, K, Lyr = w.n_seqs, w.n_v_heads, w.n_k_heads, w.state_size, w.conv_kernel, w.layers
+    layers = []
+
+    def make(l):
+        return inputs.draw_block_layer(l, w)
+
+    for l0 in range(0, Lyr, 16):
+        for l, d in zip(range(l0, min(Lyr, l0 + 16)), parallel(make, range(l0, min(Lyr, l0 + 16)))):
+            dv = {}
+            for key, val in d.items():
+                arr = np.ascontiguousarray(val)
+                if arr.dtype == np.uint16:
+                    arr = arr.view(np.int16)
+                dv[key] = torch.from_numpy(arr).cuda()
+            dv["out"] = torch.empty((N, H, S), device="cuda")
+            layers.append(dv)
+        log(f"block: {len(layers)}/{Lyr} layers resident")
+    torch.cuda.synchronize()
+
+    def step():
+        for t in layers:
+            gdn.gdn_decode_block_bf16(t["qkv"], t["z"], t["a"], t["b"], t["conv_w"], t["A_log"],
+                                      t["dt_bias"], t["norm_w"], t["conv_state"], t["state"],
+                                      t["out"], HK, w.scale, w.l2_eps, w.eps)
+
+    for _ in range(warmup):
+        step()
+    with Timer(torch) as tm:
+        for _ in range(steps):
+            step()
+    ms = tm.wall_ms / steps
+    nbytes = Lyr * block_layer_bytes(N, H, HK, S, K)
+    return {
+        "workload": "fused bf16 decode layer: 64 sequences x 48 layers, 16 -> 32 heads, S=128, "
+                    "C=8192, K=4, one launch per layer",
+        "ms_per_step": ms,
+        "launches_per_step": Lyr,
+        "GBps": nbytes / (ms * 1e-3) / 1e9,
+        "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "algorithmic_bytes_per_step": nbytes,
+    }
+
+
+def cpu_baseline(inputs, d, budget_s):
+    """The C oracle's decode recurrence on a sample of the headline batch, on
+    this host's cores. The oracle routine is called directly on arrays
+    prepared once (the test front end's defensive copies are not timed)."""
+    import ctypes
+    import oracle
+    threads = host_threads()
+    oracle.set_threads(threads)
+    lib = oracle._lib("f32")
+    w = inputs.WORKLOADS[2]
+    n, H, S = 32, w.n_v_heads, w.state_size
+    f32 = lambda x: np.ascontiguousarray(x, dtype=np.float32)
+    q = f32(oracle.l2norm_gqa(d["q_raw"][:n], H, w.l2_eps))
+    k = f32(oracle.l2norm_gqa(d["k_raw"][:n], H, w.l2_eps))
+    g = f32(oracle.decay_gate(d["a"][:n], d["dt_bias"], d["A_log"]))
+    beta = f32(oracle.sigmoid(d["b"][:n]))
+    v = f32(d["v"][:n])
+    st = f32(d["state"][:n]).copy()
+    y = np.empty_like(v)
+    P = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+
+    def run():
+        lib.oracle_recurrence_seq(P(st), P(q), P(k), P(v), P(g), P(beta), P(y), n, 1, H, S,
+                                  float(w.scale))
+
+    run()                                              # warm-up
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        run()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 10000:
+            break
+    state_bytes = 2 * n * H * S * S * 4
+    return {"value": state_bytes * reps / el / 1e9, "unit": "GB/s", "cores": oracle.get_threads(),
+            "kind": "oracle",
+            "sample": f"{n} of the 256 sequences (all 32 V-heads, S=128): {reps} decode steps "
+                      f"in {el:.1f} s; state bytes read+written per second"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the gated delta-rule path shards by sequence and "
+              "head with no exchange, and this build measures one GPU's share (use --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_attention_ssm_recurrence_amd import gdn, inputs
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    gdn.load_library()
+    legs = [s.strip() for s in args.legs.split(",") if s.strip()]
+    K, W = args.steps, args.warmup
+
+    log("leg decode: 256 x 32 x 128 recurrence")
+    w, d, dec = run_decode(torch, gdn, inputs, K, W)
+    torch.cuda.empty_cache()
+    out_legs = {}
+    if "decode_full" in legs:
+        log("leg decode_full")
+        _, _, full = run_decode(torch, gdn, inputs, K, W, with_glue=True)
+        out_legs["decode_full"] = {"ms_per_step": full["ms_per_step"],
+                                   "state_GBps": full["state_GBps"]}
+        torch.cuda.empty_cache()
+    if "scan" in legs:
+        log("leg scan: conv 4096x8192 + recurrence T=4096")
+        out_legs["scan"] = run_scan(torch, gdn, inputs, K, W)
+        torch.cuda.empty_cache()
+    if "block" in legs:
+        log("leg block: 64 seqs x 48 layers")
+        out_legs["block"] = run_block(torch, gdn, inputs, K, W)
+        torch.cuda.empty_cache()
+
+    achieved = dec["algorithmic_bytes_per_launch"] / (dec["kernel_ms_events"] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": dec["state_GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": dec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: seeded numpy PCG64 draws with the workloads' shapes and "
+                "distributions; no dataset, no trained weights",
+        "config": {"workload": dec["workload"], "n_seqs": w.n_seqs, "n_v_heads": w.n_v_heads,
+                   "n_k_heads": w.n_k_heads, "state_size": w.state_size,
+                   "state_bytes_per_step": dec["state_bytes_per_launch"]},
+        "frac_hbm_peak_state": dec["state_GBps"] / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": "recurrence_decode_kernel<128,32>",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "kernel_ms": dec["kernel_ms_events"],
+                     "bytes_per_launch": dec["algorithmic_bytes_per_launch"],
+                     "traffic": None},
+        "legs": out_legs,
+    }
+    if "scan" in out_legs:
+        line["scan_tokens_per_s"] = out_legs["scan"]["tokens_per_s"]
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {host_threads()} threads, ~{args.cpu_seconds:.0f} s")
+        line["cpu_baseline"] = cpu_baseline(inputs, d, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+/*
+ * gdn.h: C ABI of the Gated DeltaNet (gated delta-rule) SSM block on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Sources. The operations follow three pages:
+ *   [FM]  Foundry, metal/kernels/fm_kernel_ssm.m (host dispatch + MSL kernels)
+ *   [CU]  Foundry, cuda_kernels/ssm_gated_delta.cu at commit 775df8ab
+ *   [MLX] mlx-native 0.21.1, src/shaders/gated_delta_net_decode.metal
+ * Each entry point names the section that defines its operation.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is a DEVICE pointer to memory the caller allocated and
+ *     owns. The library never allocates, frees or synchronises; it enqueues
+ *     its kernels on `stream` (a hipStream_t; NULL is the default stream)
+ *     and returns at once. Faults during execution surface when the caller
+ *     synchronises the stream.
+ *   - Arrays are dense and row-major (last index fastest), fp32 unless a
+ *     parameter says bf16; bf16 values are passed as their 16-bit patterns.
+ *   - Arguments are validated before anything is enqueued: on any non-zero
+ *     return nothing was launched and no memory was touched. Shape arguments
+ *     (heads, state_size, head_dim, conv_dim, conv_kernel) must be positive.
+ *     A count argument (n_seqs, n_tokens, rows, n, n_rows) of 0 is an empty
+ *     input: the call returns GDN_OK and launches nothing, and its pointers
+ *     are not inspected (they may be NULL). A negative count is GDN_ESIZE.
+ *   - Shapes are checked before pointers: a call with both a bad shape and a
+ *     NULL pointer returns the shape's error code.
+ *   - Outputs (y, out, g, ...) must not overlap any input. State arrays are
+ *     read and written by the same thread, so they are updated in place.
+ *   - Pointers named as float4-accessed must be 16-byte aligned.
+ *   - Notation: N = n_seqs, T = n_tokens, H = n_v_heads, HK = n_k_heads,
+ *     S = state_size (key dim = value dim = head dim), C = conv_dim,
+ *     K = conv_kernel.
+ *
+ * State layout ([FM] "Delta-rule recurrence", [CU] file header "Config"):
+ *   state[n][h][j][i] (N x H x S x S floats) holds entry (i, j) of the
+ *   per-head state, i over the key dimension and j over the value dimension:
+ *   row j is S contiguous floats over i ("transposed" layout).
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define GDN_OK 0
+#define GDN_ENULL 1        /* a required pointer is NULL */
+#define GDN_ESIZE 2        /* a shape <= 0, a count < 0, too large, or sizes disagree */
+#define GDN_EUNSUPPORTED 3 /* a shape this build has no kernel for */
+#define GDN_EALIGN 4       /* a float4-accessed pointer is not 16-byte aligned */
+#define GDN_ELAUNCH 5      /* the HIP runtime rejected a kernel launch */
+
+/* Text for a return code (static storage, never NULL). */
+const char *gdn_strerror(int code);
+
+/* ABI version of this header: 1. */
+int gdn_abi_version(void);
+
+/*
+ * Decay gate ([CU] fc_ssm_decay_gate / fc_ssm_decay_gate_nx; [FM] "Decay
+ * gate"):  g[r][h] = -exp(A_log[h]) * softplus(a[r][h] + dt_bias[h]),
+ * softplus(u) = u when u > 20, else log1p(exp(u)). g <= 0, so the decay
+ * exp(g) of the recurrence lies in (0, 1].
+ *   a, g          [rows][n_heads]
+ *   dt_bias, A_log [n_heads]
+ * Errors: GDN_ENULL, GDN_ESIZE (n_heads <= 0, rows < 0), GDN_ELAUNCH.
+ */
+int gdn_decay_gate(const float *a, const float *dt_bias, const float *A_log, float *g,
+                   int n_heads, int64_t rows, void *stream);
+
+/*
+ * beta = sigmoid(x) = 1 / (1 + exp(-x)), element-wise ([CU] fc_sigmoid).
+ * y may equal x (in place); otherwise they must not overlap.
+ *   x, y [n]
+ * Errors: GDN_ENULL, GDN_ESIZE (n < 0), GDN_ELAUNCH.
+ */
+int gdn_sigmoid(const float *x, float *y, int64_t n, void *stream);
+
+/*
+ * q/k L2 normalisation with the tiled grouped-query repeat ([CU]
+ * fc_ssm_qknorm_gqa / _nx; [MLX] "GQA: tiled mapping"):
+ *   xhat = x / max(||x||_2, eps) per K-head; out[r][vh] = xhat[r][vh mod HK].
+ *   x   [rows][n_k_heads][head_dim]      (float4-accessed)
+ *   out [rows][n_v_heads][head_dim]      (float4-accessed)
+ * Errors: GDN_ENULL; GDN_ESIZE (a shape <= 0, rows < 0, n_v_heads not a multiple of
+ * n_k_heads); GDN_EUNSUPPORTED (head_dim not a multiple of 4 or > 1024);
+ * GDN_EALIGN; GDN_ELAUNCH.
+ */
+int gdn_l2norm_gqa(const float *x, float *out, int64_t rows, int n_k_heads, int n_v_heads,
+                   int head_dim, float eps, void *stream);
+
+/*
+ * Causal depthwise conv1d + SiLU, one decode step per sequence ([FM]
+ * "Causal depthwise conv1d + SiLU", fmssm_conv1d_silu; [CU] Kernel 2 and
+ * fc_ssm_conv1d_silu_slots). Per channel c of sequence n, with
+ * hist = conv_state[n][c][0..K-2] (oldest first):
+ *   acc = x[n][c] * w[c][K-1] + sum_{u=0..K-2} hist[u] * w[c][u]
+ *   out[n][c] = acc / (1 + exp(-acc))
+ * then hist drops its oldest entry and appends the raw x[n][c].
+ *   x, out     [n_seqs][conv_dim]
+ *   w          [conv_dim][conv_kernel]
+ *   conv_state [n_seqs][conv_dim][conv_kernel - 1]   (updated in place)
+ * Errors: GDN_ENULL, GDN_ESIZE, GDN_EUNSUPPORTED (conv_kernel not in 2..4),
+ * GDN_ELAUNCH.
+ */
+int gdn_conv1d_silu(const float *x, const float *w, float *conv_state, float *out, int n_seqs,
+                    int conv_dim, int conv_kernel, void *stream);
+
+/*
+ * The same conv over n_tokens positions of each sequence ([FM]
+ * fmssm_conv1d_silu_seq; [CU] fc_ssm_conv1d_silu_seq). Every position's
+ * output and the final conv_state equal n_tokens single steps bit for bit.
+ *   x, out [n_seqs][n_tokens][conv_dim]
+ * Other arguments and errors as gdn_conv1d_silu.
+ */
+int gdn_conv1d_silu_seq(const float *x, const float *w, float *conv_state, float *out,
+                        int n_seqs, int n_tokens, int conv_dim, int conv_kernel, void *stream);
+
+/*
+ * Gated delta-rule recurrence, one token per sequence (decode). [FM]
+ * "Delta-rule recurrence" (fmssm_recurrence), [CU] Kernel 1 and
+ * fc_ssm_recurrence_slots, [MLX] "Mathematical recurrence". For every
+ * (n, h) and every state row j, with r the row and d = exp(g[n][h]):
+ *   r = d * r;  pred = r . k;  delta = (v[j] - pred) * beta[n][h];
+ *   r = r + k * delta;  y[j] = scale * (r . q)    (read after the update)
+ *   state      [n_seqs][n_v_heads][S][S]  (updated in place; float4-accessed)
+ *   q, k, v, y [n_seqs][n_v_heads][S]     (q, k after any GQA repeat;
+ *                                          q, k float4-accessed)
+ *   g, beta    [n_seqs][n_v_heads]        (g <= 0 from gdn_decay_gate)
+ * scale multiplies the read-out sum (1/sqrt(S) for the model).
+ * Errors: GDN_ENULL, GDN_ESIZE, GDN_EUNSUPPORTED (state_size not in
+ * {32, 64, 128, 256}), GDN_EALIGN, GDN_ELAUNCH.
+ */
+int gdn_recurrence(float *state, const float *q, const float *k, const float *v, const float *g,
+                   const float *beta, float *y, int n_seqs, int n_v_heads, int state_size,
+                   float scale, void *stream);
+
+/*
+ * The recurrence over n_tokens positions of each sequence, the state held
+ * on chip between positions and written back once ([FM]
+ * fmssm_recurrence_seq; [CU] fc_ssm_recurrence_seq; [MLX] token loop).
+ * Every y and the final state equal n_tokens calls of gdn_recurrence bit
+ * for bit.
+ *   state      [n_seqs][n_v_heads][S][S]            (updated in place)
+ *   q, k, v, y [n_seqs][n_tokens][n_v_heads][S]
+ *   g, beta    [n_seqs][n_tokens][n_v_heads]
+ * Errors as gdn_recurrence.
+ */
+int gdn_recurrence_seq(float *state, const float *q, const float *k, const float *v,
+                       const float *g, const float *beta, float *y, int n_seqs, int n_tokens,
+                       int n_v_heads, int state_size, float scale, void *stream);
+
+/*
+ * Gated RMSNorm ([FM] "Gated RMSNorm"; [CU] Kernel 3): per row of head_dim
+ * values, out = y / sqrt(mean(y^2) + eps) * w * silu(z), silu(z) =
+ * z / (1 + exp(-z)). The weight is shared by every row (every head).
+ *   y, z, out [n_rows][head_dim]   w [head_dim]   (all float4-accessed)
+ * Errors: GDN_ENULL, GDN_ESIZE, GDN_EUNSUPPORTED (head_dim not a multiple
+ * of 4 or > 1024), GDN_EALIGN, GDN_ELAUNCH.
+ */
+int gdn_gated_rmsnorm(const float *y, const float *w, const float *z, float *out,
+                      int64_t n_rows, int head_dim, float eps, void *stream);
+
+/*
+ * One decode layer of the block, fused into one kernel: bf16 activations,
+ * fp32 state. The per-token order of [CU]'s decode path (its file header and
+ * "glue" kernels) with the grouped-query repeat done by index ([MLX]):
+ *   1. conv1d + SiLU one step on the widened qkv[n] (all C channels),
+ *      rolling conv_state[n];
+ *   2. split the conv output as [q: HK*S | k: HK*S | v: H*S];
+ *   3. L2-normalise q and k per K-head (l2_eps); V-head vh reads K-head
+ *      vh mod HK;
+ *   4. beta = sigmoid(b[n][vh]); g = -exp(A_log[vh]) *
+ *      softplus(a[n][vh] + dt_bias[vh]);
+ *   5. one recurrence step of state[n][vh], y = scale * (row . q);
+ *   6. out[n][vh] = gated RMSNorm(y[vh], norm_w, widened z[n][vh], eps).
+ *   qkv        [n_seqs][C] bf16, C = 2*HK*S + H*S
+ *   z          [n_seqs][n_v_heads][S] bf16
+ *   a, b       [n_seqs][n_v_heads]
+ *   conv_w     [C][conv_kernel];  A_log, dt_bias [n_v_heads];  norm_w [S]
+ *   conv_state [n_seqs][C][conv_kernel - 1]   (updated in place)
+ *   state      [n_seqs][n_v_heads][S][S]      (updated in place)
+ *   out        [n_seqs][n_v_heads][S]
+ * Errors: GDN_ENULL; GDN_ESIZE (a size <= 0 or H not a multiple of HK);
+ * GDN_EUNSUPPORTED (S != 128, H/HK > 4, conv_kernel not in 2..4);
+ * GDN_EALIGN (state, norm_w or out not 16-byte aligned); GDN_ELAUNCH.
+ */
+int gdn_decode_block_bf16(const uint16_t *qkv, const uint16_t *z, const float *a,
+                          const float *b, const float *conv_w, const float *A_log,
+                          const float *dt_bias, const float *norm_w, float *conv_state,
+                          float *state, float *out, int n_seqs, int n_k_heads, int n_v_heads,
+                          int state_size, int conv_kernel, float scale, float l2_eps, float eps,
+                          void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,163 @@
+// Causal depthwise conv1d + SiLU on gfx950, one step (decode) and over many
+// positions (scan).
+//
+// Per channel c the window is the K-1 stored inputs (oldest first) followed by
+// the current input; the sum starts from the newest tap, x * w[c][K-1], then
+// adds history[u] * w[c][u] in ascending u, and the output is SiLU of the sum.
+// The history then drops its oldest entry and appends the raw input (Foundry
+// fm_kernel_ssm.m "Causal depthwise conv1d + SiLU"; ssm_gated_delta.cu
+// Kernel 2 and fc_ssm_conv1d_silu_seq).
+//
+// The history is nothing but the last K-1 raw inputs, so no output depends on
+// an earlier output: the scan is data-parallel over positions as well as over
+// channels. Each thread takes one channel and a chunk of positions, reading
+// K-1 inputs before its chunk as a halo (from conv_state for positions before
+// the first). Both kernels evaluate each position with the same conv_point,
+// so the scan and single steps agree bit for bit.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+
+template <int K>
+__global__ __launch_bounds__(256) void conv_step_kernel(const float* __restrict__ x,
+                                                        const float* __restrict__ w,
+                                                        float* __restrict__ conv_state,
+                                                        float* __restrict__ out, int64_t total,
+                                                        int conv_dim) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // n * C + c
+  if (idx >= total) return;
+  const int c = (int)(idx % conv_dim);
+  float wc[K], hist[K - 1];
+#pragma unroll
+  for (int u = 0; u < K; ++u) wc[u] = w[(int64_t)c * K + u];
+  float* cs = conv_state + idx * (K - 1);
+#pragma unroll
+  for (int u = 0; u < K - 1; ++u) hist[u] = cs[u];
+  const float xv = x[idx];
+  out[idx] = conv_point<K>(xv, hist, wc);
+#pragma unroll
+  for (int u = 0; u + 1 < K - 1; ++u) cs[u] = hist[u + 1];
+  cs[K - 2] = xv;
+}
+
+// Scan: block (cb, chunk, n) covers channels cb*256 .. +255 and positions
+// chunk*TB .. +TB-1 of sequence n.
+template <int K, int TB>
+__global__ __launch_bounds__(256) void conv_scan_kernel(const float* __restrict__ x,
+                                                        const float* __restrict__ w,
+                                                        float* __restrict__ conv_state,
+                                                        float* __restrict__ out, int n_tokens,
+                                                        int conv_dim, int c_blocks,
+                                                        int t_chunks) {
+  const int cb = blockIdx.x % c_blocks;
+  const int chunk = (blockIdx.x / c_blocks) % t_chunks;
+  const int64_t n = blockIdx.x / ((int64_t)c_blocks * t_chunks);
+  const int c = cb * 256 + threadIdx.x;
+  if (c >= conv_dim) return;
+  const int t0 = chunk * TB;
+  const int t1 = min(t0 + TB, n_tokens);
+  const float* xc = x + n * (int64_t)n_tokens * conv_dim + c;
+  float* oc = out + n * (int64_t)n_tokens * conv_dim + c;
+  float* cs = conv_state + (n * conv_dim + c) * (K - 1);
+
+  float wc[K];
+#pragma unroll
+  for (int u = 0; u < K; ++u) wc[u] = w[(int64_t)c * K + u];
+
+  // hist = inputs at positions t0-K+1 .. t0-1 (negative positions: conv_state)
+  float hist[K - 1];
+#pragma unroll
+  for (int u = 0; u < K - 1; ++u) {
+    const int t = t0 - (K - 1) + u;
+    hist[u] = t < 0 ? cs[K - 1 + t] : xc[(int64_t)t * conv_dim];
+  }
+  // The chunk-0 thread is the only reader of the old conv_state, so it also
+  // writes the new one: the last K-1 entries of (old history ++ inputs).
+  float fin[K - 1];
+  if (chunk == 0) {
+#pragma unroll
+    for (int u = 0; u < K - 1; ++u) {
+      const int t = n_tokens - (K - 1) + u;
+      fin[u] = t < 0 ? cs[K - 1 + t] : xc[(int64_t)t * conv_dim];
+    }
+  }
+  for (int t = t0; t < t1; ++t) {
+    const float xv = xc[(int64_t)t * conv_dim];
+    oc[(int64_t)t * conv_dim] = conv_point<K>(xv, hist, wc);
+#pragma unroll
+    for (int u = 0; u + 1 < K - 1; ++u) hist[u] = hist[u + 1];
+    hist[K - 2] = xv;
+  }
+  if (chunk == 0) {
+#pragma unroll
+    for (int u = 0; u < K - 1; ++u) cs[u] = fin[u];
+  }
+}
+
+static int check_conv(const float* x, const float* w, float* conv_state, float* out, int n_seqs,
+                      int n_tokens, int conv_dim, int conv_kernel) {
+  if (n_seqs < 0 || n_tokens < 0 || conv_dim <= 0 || conv_kernel <= 0) return GDN_ESIZE;
+  if (conv_kernel < 2 || conv_kernel > 4) return GDN_EUNSUPPORTED;
+  if (n_seqs == 0 || n_tokens == 0) return kNothingToDo;
+  if (!x || !w || !conv_state || !out) return GDN_ENULL;
+  int64_t a, b;
+  if (!mul_ok(n_seqs, n_tokens, &a) || !mul_ok(a, conv_dim, &b)) return GDN_ESIZE;
+  if (!mul_ok((int64_t)n_seqs * conv_dim, conv_kernel, &a)) return GDN_ESIZE;
+  return GDN_OK;
+}
+
+template <int K>
+static int launch_conv_step(const float* x, const float* w, float* cs, float* out, int n_seqs,
+                            int conv_dim, hipStream_t s) {
+  const int64_t total = (int64_t)n_seqs * conv_dim;
+  if (grid_for(total, 256) == 0 || total / 256 >= (int64_t(1) << 31)) return GDN_ESIZE;
+  hipLaunchKernelGGL((conv_step_kernel<K>), dim3(grid_for(total, 256)), dim3(256), 0, s, x, w, cs,
+                     out, total, conv_dim);
+  return launch_status();
+}
+
+template <int K>
+static int launch_conv_scan(const float* x, const float* w, float* cs, float* out, int n_seqs,
+                            int n_tokens, int conv_dim, hipStream_t s) {
+  constexpr int TB = 16;
+  const int c_blocks = (conv_dim + 255) / 256;
+  const int t_chunks = (n_tokens + TB - 1) / TB;
+  const int64_t blocks = (int64_t)n_seqs * c_blocks * t_chunks;
+  if (blocks >= (int64_t(1) << 31)) return GDN_ESIZE;
+  hipLaunchKernelGGL((conv_scan_kernel<K, TB>), dim3((unsigned)blocks), dim3(256), 0, s, x, w, cs,
+                     out, n_tokens, conv_dim, c_blocks, t_chunks);
+  return launch_status();
+}
+
+}  // namespace gdn
+
+using namespace gdn;
+
+extern "C" int gdn_conv1d_silu(const float* x, const float* w, float* conv_state, float* out,
+                               int n_seqs, int conv_dim, int conv_kernel, void* stream) {
+  const int rc = check_conv(x, w, conv_state, out, n_seqs, 1, conv_dim, conv_kernel);
+  if (rc != GDN_OK) return finish_check(rc);
+  hipStream_t s = as_stream(stream);
+  switch (conv_kernel) {
+    case 2: return launch_conv_step<2>(x, w, conv_state, out, n_seqs, conv_dim, s);
+    case 3: return launch_conv_step<3>(x, w, conv_state, out, n_seqs, conv_dim, s);
+    case 4: return launch_conv_step<4>(x, w, conv_state, out, n_seqs, conv_dim, s);
+  }
+  return GDN_EUNSUPPORTED;
+}
+
+extern "C" int gdn_conv1d_silu_seq(const float* x, const float* w, float* conv_state, float* out,
+                                   int n_seqs, int n_tokens, int conv_dim, int conv_kernel,
+                                   void* stream) {
+  const int rc = check_conv(x, w, conv_state, out, n_seqs, n_tokens, conv_dim, conv_kernel);
+  if (rc != GDN_OK) return finish_check(rc);
+  hipStream_t s = as_stream(stream);
+  switch (conv_kernel) {
+    case 2: return launch_conv_scan<2>(x, w, conv_state, out, n_seqs, n_tokens, conv_dim, s);
+    case 3: return launch_conv_scan<3>(x, w, conv_state, out, n_seqs, n_tokens, conv_dim, s);
+    case 4: return launch_conv_scan<4>(x, w, conv_state, out, n_seqs, n_tokens, conv_dim, s);
+  }
+  return GDN_EUNSUPPORTED;
+}

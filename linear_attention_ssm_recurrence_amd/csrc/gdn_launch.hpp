@@ -1,0 +1,44 @@
+// Host-side helpers shared by the C-ABI entry points: argument checks and the
+// launch error check. Every entry point validates all of its arguments before
+// it enqueues anything, so a non-zero return means nothing was launched.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+// Internal result of an argument check: valid, but there is no work (a zero
+// count). The entry point returns GDN_OK without launching anything.
+constexpr int kNothingToDo = -1;
+
+inline int finish_check(int rc) { return rc == kNothingToDo ? GDN_OK : rc; }
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool is_state_size(int s) { return s == 32 || s == 64 || s == 128 || s == 256; }
+
+// Largest element count any single array may have: keeps every flattened
+// index inside int64 with room, and every grid inside the launch limits.
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+inline bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > kMaxElems / a) return false;
+  *out = a * b;
+  return true;
+}
+
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ELAUNCH;
+}
+
+inline unsigned grid_for(int64_t items, int per_block) {
+  return (unsigned)((items + per_block - 1) / per_block);
+}
+
+}  // namespace gdn

@@ -1,0 +1,299 @@
+// Gated delta-rule recurrence on gfx950: decode (one token per sequence) and
+// the sequential scan (many tokens, state held in VGPRs).
+//
+// The rule, per (sequence, V-head, value row j) and token, is the one of
+// Foundry fm_kernel_ssm.m "Delta-rule recurrence", ssm_gated_delta.cu
+// Kernel 1 and mlx-native gated_delta_net_decode.metal "Mathematical
+// recurrence": decay the row by exp(g), predict pred = row . k, correct by
+// delta = (v_j - pred) * beta with the rank-1 update row += k * delta, and
+// read out y_j = scale * (row . q) after the update.
+//
+// Work mapping (wave64). A state row of S floats is spread over L = S/E
+// lanes, E floats per lane (gdn_device.hpp); a wave covers G = 64/L rows per
+// float4 instruction. Both kernels call the same delta_rule_step with the
+// same E and L, so a scan over T tokens and T decode launches produce the
+// same bits. Reductions are DPP butterflies inside a 16-lane row (plus one
+// ds_swizzle when L = 32): no LDS and no barrier on the per-token path.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+// ---------------------------------------------------------------------------
+// Decode: each wave owns RW consecutive rows of one (sequence, head). It
+// issues every state load of its rows first (RW/G * E/4 float4 loads per
+// lane, all independent), then runs the step row-group by row-group and
+// streams the rows back. k and q of the head are loaded once per wave and
+// reused for all its rows; g and beta are wave-uniform.
+// ---------------------------------------------------------------------------
+template <int S, int RW>
+__global__ __launch_bounds__(256) void recurrence_decode_kernel(
+    float* __restrict__ state, const float* __restrict__ q, const float* __restrict__ k,
+    const float* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
+    float* __restrict__ y, int64_t n_pairs, float scale) {
+  using Lay = RecurLayout<S>;
+  constexpr int E = Lay::E, L = Lay::L, G = Lay::G;
+  constexpr int IT = RW / G;         // row groups per wave
+  constexpr int WPH = S / RW;        // waves per (sequence, head)
+  static_assert(RW % G == 0 && S % RW == 0, "rows per wave must tile the head");
+
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t pair = wave / WPH;
+  if (pair >= n_pairs) return;  // uniform across the wave; the kernel has no barrier
+  const int p = lane % L;
+  const int row0 = (int)(wave % WPH) * RW + lane / L;
+
+  float kk[E], qq[E];
+  load_row_part<E, L>(k + pair * S, p, kk);
+  load_row_part<E, L>(q + pair * S, p, qq);
+  const float d = expf(g[pair]);
+  const float b = beta[pair];
+
+  float* sp = state + pair * (int64_t)S * S;
+  float4 raw[IT][E / 4];
+#pragma unroll
+  for (int it = 0; it < IT; ++it)
+#pragma unroll
+    for (int m = 0; m < E / 4; ++m)
+      raw[it][m] = load4_stream(sp + (int64_t)(row0 + it * G) * S + 4 * (p + L * m));
+  float vv[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) vv[it] = v[pair * S + row0 + it * G];
+
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    float r[E];
+    unpack<E>(raw[it], r);
+    const float yj = delta_rule_step<E, L>(r, kk, qq, vv[it], d, b, scale);
+    float* rp = sp + (int64_t)(row0 + it * G) * S;
+#pragma unroll
+    for (int m = 0; m < E / 4; ++m)
+      store4_stream(rp + 4 * (p + L * m), make_float4(r[4 * m], r[4 * m + 1], r[4 * m + 2], r[4 * m + 3]));
+    if (p == 0) y[pair * S + row0 + it * G] = yj;
+  }
+}
+
+template <int S>
+struct DecodeCfg;
+template <> struct DecodeCfg<32> { static constexpr int RW = 32; };
+template <> struct DecodeCfg<64> { static constexpr int RW = 32; };
+template <> struct DecodeCfg<128> { static constexpr int RW = 32; };
+template <> struct DecodeCfg<256> { static constexpr int RW = 16; };
+
+template <int S>
+static int launch_decode(float* state, const float* q, const float* k, const float* v,
+                         const float* g, const float* beta, float* y, int64_t n_pairs,
+                         float scale, hipStream_t stream) {
+  constexpr int RW = DecodeCfg<S>::RW;
+  constexpr int WAVES_PER_BLOCK = 4;
+  const int64_t waves = n_pairs * (S / RW);
+  const unsigned blocks = grid_for(waves, WAVES_PER_BLOCK);
+  hipLaunchKernelGGL((recurrence_decode_kernel<S, RW>), dim3(blocks), dim3(64 * WAVES_PER_BLOCK),
+                     0, stream, state, q, k, v, g, beta, y, n_pairs, scale);
+  return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// Scan: a block of W waves owns R = W*G consecutive rows of one (sequence,
+// head) and carries them in VGPRs through all tokens. Per chunk of CT tokens
+// the block stages k and q of its head, v of its rows, and exp(g) and beta
+// into LDS; the next chunk's global loads are issued before the current chunk
+// is computed and land in the other LDS buffer, so there is one barrier per
+// chunk and none per token. exp(g) is evaluated once per token per block (by
+// the staging thread), not once per lane.
+// ---------------------------------------------------------------------------
+template <int S>
+struct ScanCfg {
+  using Lay = RecurLayout<S>;
+  static constexpr int W = (S / Lay::G) < 4 ? (S / Lay::G) : 4;  // waves per block
+  static constexpr int R = W * Lay::G;                            // rows per block
+  static constexpr int BPH = S / R;                               // blocks per head
+  static constexpr int CT = S >= 256 ? 16 : 32;                   // tokens per chunk
+  static constexpr int THREADS = 64 * W;
+  // LDS words of one chunk buffer: k, q [CT][S], v [CT][R], decay, beta [CT]
+  static constexpr int KQ = CT * S;
+  static constexpr int BUF = 2 * KQ + CT * R + 2 * CT;
+  // float4 loads of k and q per thread per chunk (each of k and q)
+  static constexpr int KQ4 = KQ / 4 / THREADS;
+  static constexpr int VPT = (CT * R + THREADS - 1) / THREADS;    // v loads per thread
+  static_assert(KQ % (4 * THREADS) == 0, "k/q chunk must split evenly into float4 per thread");
+  static_assert(CT <= THREADS, "one staging thread per token");
+};
+
+template <int S>
+__global__ __launch_bounds__(ScanCfg<S>::THREADS) void recurrence_scan_kernel(
+    float* __restrict__ state, const float* __restrict__ q, const float* __restrict__ k,
+    const float* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
+    float* __restrict__ y, int n_tokens, int n_v_heads, float scale) {
+  using Lay = RecurLayout<S>;
+  using Cfg = ScanCfg<S>;
+  constexpr int E = Lay::E, L = Lay::L, G = Lay::G;
+  constexpr int CT = Cfg::CT, R = Cfg::R, KQ = Cfg::KQ, BUF = Cfg::BUF, THREADS = Cfg::THREADS;
+  __shared__ float smem[2 * BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int p = lane % L;
+  const int64_t head = blockIdx.x / Cfg::BPH;          // n * H + h
+  const int rblk = (int)(blockIdx.x % Cfg::BPH) * R;    // first row of the block
+  const int64_t n = head / n_v_heads;
+  const int h = (int)(head % n_v_heads);
+  const int lrow = wv * G + lane / L;                   // row within the block
+  const int row = rblk + lrow;
+
+  const int64_t tok_stride = (int64_t)n_v_heads * S;     // q/k/v/y stride per token
+  const int64_t base_n = n * (int64_t)n_tokens;          // token index of (n, 0)
+  const float* qn = q + base_n * tok_stride + (int64_t)h * S;
+  const float* kn = k + base_n * tok_stride + (int64_t)h * S;
+  const float* vn = v + base_n * tok_stride + (int64_t)h * S + rblk;
+  float* yn = y + base_n * tok_stride + (int64_t)h * S + row;
+  const float* gn = g + base_n * n_v_heads + h;
+  const float* bn = beta + base_n * n_v_heads + h;
+
+  // Registers that carry one chunk from global memory to LDS.
+  float4 pk[Cfg::KQ4], pq[Cfg::KQ4];
+  float pv[Cfg::VPT];
+  float pdec = 0.0f, pbeta = 0.0f;
+
+  auto fetch = [&](int t0) {
+    const int ct = min(CT, n_tokens - t0);
+#pragma unroll
+    for (int i = 0; i < Cfg::KQ4; ++i) {
+      const int f = (i * THREADS + tid) * 4;   // float index inside [CT][S]
+      const int tt = f / S, col = f % S;
+      if (tt < ct) {
+        pk[i] = load4(kn + (int64_t)(t0 + tt) * tok_stride + col);
+        pq[i] = load4(qn + (int64_t)(t0 + tt) * tok_stride + col);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::VPT; ++i) {
+      const int f = i * THREADS + tid;         // index inside [CT][R]
+      const int tt = f / R, rr = f % R;
+      if (f < CT * R && tt < ct) pv[i] = vn[(int64_t)(t0 + tt) * tok_stride + rr];
+    }
+    if (tid < ct) {
+      pdec = expf(gn[(int64_t)(t0 + tid) * n_v_heads]);
+      pbeta = bn[(int64_t)(t0 + tid) * n_v_heads];
+    }
+  };
+  auto deposit = [&](float* buf, int t0) {
+    const int ct = min(CT, n_tokens - t0);
+#pragma unroll
+    for (int i = 0; i < Cfg::KQ4; ++i) {
+      const int f = (i * THREADS + tid) * 4;
+      if (f / S < ct) {
+        store4(buf + f, pk[i]);
+        store4(buf + KQ + f, pq[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::VPT; ++i) {
+      const int f = i * THREADS + tid;
+      if (f < CT * R && f / R < ct) buf[2 * KQ + f] = pv[i];
+    }
+    if (tid < ct) {
+      buf[2 * KQ + CT * R + tid] = pdec;
+      buf[2 * KQ + CT * R + CT + tid] = pbeta;
+    }
+  };
+
+  float r[E];
+  float* srow = state + head * (int64_t)S * S + (int64_t)row * S;
+  load_row_part<E, L>(srow, p, r);
+
+  fetch(0);
+  deposit(smem, 0);
+  __syncthreads();
+
+  int buf_id = 0;
+  for (int t0 = 0; t0 < n_tokens; t0 += CT) {
+    const int ct = min(CT, n_tokens - t0);
+    const bool more = t0 + CT < n_tokens;
+    if (more) fetch(t0 + CT);
+    const float* buf = smem + buf_id * BUF;
+    for (int tt = 0; tt < ct; ++tt) {
+      float kk[E], qq[E];
+      load_row_part<E, L>(buf + tt * S, p, kk);
+      load_row_part<E, L>(buf + KQ + tt * S, p, qq);
+      const float vj = buf[2 * KQ + tt * R + lrow];
+      const float d = buf[2 * KQ + CT * R + tt];
+      const float b = buf[2 * KQ + CT * R + CT + tt];
+      const float yj = delta_rule_step<E, L>(r, kk, qq, vj, d, b, scale);
+      if (p == 0) yn[(int64_t)(t0 + tt) * tok_stride] = yj;
+    }
+    if (more) deposit(smem + (buf_id ^ 1) * BUF, t0 + CT);
+    __syncthreads();
+    buf_id ^= 1;
+  }
+
+#pragma unroll
+  for (int m = 0; m < E / 4; ++m)
+    store4(srow + 4 * (p + L * m), make_float4(r[4 * m], r[4 * m + 1], r[4 * m + 2], r[4 * m + 3]));
+}
+
+template <int S>
+static int launch_scan(float* state, const float* q, const float* k, const float* v,
+                       const float* g, const float* beta, float* y, int n_seqs, int n_tokens,
+                       int n_v_heads, float scale, hipStream_t stream) {
+  using Cfg = ScanCfg<S>;
+  const int64_t blocks = (int64_t)n_seqs * n_v_heads * Cfg::BPH;
+  hipLaunchKernelGGL((recurrence_scan_kernel<S>), dim3((unsigned)blocks), dim3(Cfg::THREADS), 0,
+                     stream, state, q, k, v, g, beta, y, n_tokens, n_v_heads, scale);
+  return launch_status();
+}
+
+static int check_recurrence(float* state, const float* q, const float* k, const float* v,
+                            const float* g, const float* beta, float* y, int n_seqs,
+                            int n_tokens, int n_v_heads, int state_size) {
+  if (n_seqs < 0 || n_tokens < 0 || n_v_heads <= 0 || state_size <= 0) return GDN_ESIZE;
+  if (!is_state_size(state_size)) return GDN_EUNSUPPORTED;
+  if (n_seqs == 0 || n_tokens == 0) return kNothingToDo;
+  if (!state || !q || !k || !v || !g || !beta || !y) return GDN_ENULL;
+  int64_t pairs, st, vec;
+  if (!mul_ok(n_seqs, n_v_heads, &pairs) || !mul_ok(pairs, (int64_t)state_size * state_size, &st) ||
+      !mul_ok(pairs * n_tokens, state_size, &vec))
+    return GDN_ESIZE;
+  if (pairs * (state_size / 16) >= (int64_t(1) << 31)) return GDN_ESIZE;  // grid limit
+  if (!aligned16(state) || !aligned16(q) || !aligned16(k)) return GDN_EALIGN;
+  return GDN_OK;
+}
+
+}  // namespace gdn
+
+using namespace gdn;
+
+extern "C" int gdn_recurrence(float* state, const float* q, const float* k, const float* v,
+                              const float* g, const float* beta, float* y, int n_seqs,
+                              int n_v_heads, int state_size, float scale, void* stream) {
+  const int rc = check_recurrence(state, q, k, v, g, beta, y, n_seqs, 1, n_v_heads, state_size);
+  if (rc != GDN_OK) return finish_check(rc);
+  const int64_t pairs = (int64_t)n_seqs * n_v_heads;
+  hipStream_t s = as_stream(stream);
+  switch (state_size) {
+    case 32: return launch_decode<32>(state, q, k, v, g, beta, y, pairs, scale, s);
+    case 64: return launch_decode<64>(state, q, k, v, g, beta, y, pairs, scale, s);
+    case 128: return launch_decode<128>(state, q, k, v, g, beta, y, pairs, scale, s);
+    case 256: return launch_decode<256>(state, q, k, v, g, beta, y, pairs, scale, s);
+  }
+  return GDN_EUNSUPPORTED;
+}
+
+extern "C" int gdn_recurrence_seq(float* state, const float* q, const float* k, const float* v,
+                                  const float* g, const float* beta, float* y, int n_seqs,
+                                  int n_tokens, int n_v_heads, int state_size, float scale,
+                                  void* stream) {
+  const int rc =
+      check_recurrence(state, q, k, v, g, beta, y, n_seqs, n_tokens, n_v_heads, state_size);
+  if (rc != GDN_OK) return finish_check(rc);
+  hipStream_t s = as_stream(stream);
+  switch (state_size) {
+    case 32: return launch_scan<32>(state, q, k, v, g, beta, y, n_seqs, n_tokens, n_v_heads, scale, s);
+    case 64: return launch_scan<64>(state, q, k, v, g, beta, y, n_seqs, n_tokens, n_v_heads, scale, s);
+    case 128: return launch_scan<128>(state, q, k, v, g, beta, y, n_seqs, n_tokens, n_v_heads, scale, s);
+    case 256: return launch_scan<256>(state, q, k, v, g, beta, y, n_seqs, n_tokens, n_v_heads, scale, s);
+  }
+  return GDN_EUNSUPPORTED;
+}

@@ -1,0 +1,141 @@
+"""The C-ABI library on the host: it loads, exports every symbol gdn.h
+declares, and rejects bad arguments before launching anything.
+
+No call here reaches a kernel launch: every argument set fails validation (or
+is an empty input, which returns before any HIP call), so these tests need no
+GPU and are safe on one.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_ssm_recurrence_amd import build as hipbuild
+from linear_attention_ssm_recurrence_amd import gdn
+
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced
+FAKE_MIS = ctypes.c_void_p(0x10004)    # not 16-byte aligned, never dereferenced
+NUL = None
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.LIB_PATH):
+        hipbuild.build()
+    return gdn.load_library()
+
+
+def test_exports_every_header_symbol(lib):
+    names = gdn.header_symbols()
+    assert len(names) == 11, names
+    out = os.popen(f"nm -D --defined-only {gdn.LIB_PATH}").read()
+    exported = set(re.findall(r"\sT\s(gdn_\w+)", out))
+    for name in names:
+        assert name in exported, f"{name} declared in gdn.h but not exported"
+        assert hasattr(lib, name)
+
+
+def test_version_and_strerror(lib):
+    assert lib.gdn_abi_version() == 1
+    for code in range(6):
+        assert gdn.strerror(code)
+    assert "unknown" in gdn.strerror(99)
+
+
+def rec(lib, state=FAKE, q=FAKE, k=FAKE, n_seqs=1, H=2, S=32, seq=False, T=1):
+    f = lib.gdn_recurrence_seq if seq else lib.gdn_recurrence
+    args = [state, q, k, FAKE, FAKE, FAKE, FAKE, n_seqs] + ([T] if seq else []) + [H, S, 1.0, NUL]
+    return f(*args)
+
+
+@pytest.mark.parametrize("seq", [False, True])
+def test_recurrence_validation(lib, seq):
+    assert rec(lib, state=NUL, seq=seq) == gdn.GDN_ENULL
+    assert rec(lib, n_seqs=-1, seq=seq) == gdn.GDN_ESIZE
+    assert rec(lib, H=0, seq=seq) == gdn.GDN_ESIZE
+    assert rec(lib, S=0, seq=seq) == gdn.GDN_ESIZE
+    for bad_s in (16, 48, 96, 512):
+        assert rec(lib, S=bad_s, seq=seq) == gdn.GDN_EUNSUPPORTED
+    assert rec(lib, state=FAKE_MIS, seq=seq) == gdn.GDN_EALIGN
+    assert rec(lib, q=FAKE_MIS, seq=seq) == gdn.GDN_EALIGN
+    # bad shape wins over a NULL pointer
+    assert rec(lib, state=NUL, S=48, seq=seq) == gdn.GDN_EUNSUPPORTED
+    # empty inputs: no work, pointers not inspected
+    assert rec(lib, state=NUL, q=NUL, k=NUL, n_seqs=0, seq=seq) == gdn.GDN_OK
+    if seq:
+        assert rec(lib, T=0, seq=True) == gdn.GDN_OK
+        assert rec(lib, T=-3, seq=True) == gdn.GDN_ESIZE
+    # sizes whose flattened element count overflows the library's limit
+    assert rec(lib, n_seqs=2**30, H=2**20, S=256, seq=seq) == gdn.GDN_ESIZE
+
+
+@pytest.mark.parametrize("fn", ["gdn_conv1d_silu", "gdn_conv1d_silu_seq"])
+def test_conv_validation(lib, fn):
+    f = getattr(lib, fn)
+    seq = fn.endswith("_seq")
+
+    def call(x=FAKE, n=1, T=1, C=8, K=4):
+        args = [x, FAKE, FAKE, FAKE, n] + ([T] if seq else []) + [C, K, NUL]
+        return f(*args)
+
+    assert call(x=NUL) == gdn.GDN_ENULL
+    assert call(n=-1) == gdn.GDN_ESIZE
+    assert call(C=0) == gdn.GDN_ESIZE
+    assert call(K=0) == gdn.GDN_ESIZE
+    for K in (1, 5, 8):
+        assert call(K=K) == gdn.GDN_EUNSUPPORTED
+    assert call(x=NUL, n=0) == gdn.GDN_OK
+    if seq:
+        assert call(T=-1) == gdn.GDN_ESIZE
+        assert call(x=NUL, T=0) == gdn.GDN_OK
+
+
+def test_pointwise_validation(lib):
+    assert lib.gdn_decay_gate(NUL, FAKE, FAKE, FAKE, 4, 1, NUL) == gdn.GDN_ENULL
+    assert lib.gdn_decay_gate(FAKE, FAKE, FAKE, FAKE, 0, 1, NUL) == gdn.GDN_ESIZE
+    assert lib.gdn_decay_gate(FAKE, FAKE, FAKE, FAKE, 4, -1, NUL) == gdn.GDN_ESIZE
+    assert lib.gdn_decay_gate(NUL, NUL, NUL, NUL, 4, 0, NUL) == gdn.GDN_OK
+    assert lib.gdn_sigmoid(NUL, FAKE, 3, NUL) == gdn.GDN_ENULL
+    assert lib.gdn_sigmoid(FAKE, FAKE, -3, NUL) == gdn.GDN_ESIZE
+    assert lib.gdn_sigmoid(NUL, NUL, 0, NUL) == gdn.GDN_OK
+    l2 = lib.gdn_l2norm_gqa
+    assert l2(NUL, FAKE, 1, 2, 4, 32, 1e-6, NUL) == gdn.GDN_ENULL
+    assert l2(FAKE, FAKE, 1, 3, 4, 32, 1e-6, NUL) == gdn.GDN_ESIZE      # 4 % 3 != 0
+    assert l2(FAKE, FAKE, 1, 2, 4, 30, 1e-6, NUL) == gdn.GDN_EUNSUPPORTED
+    assert l2(FAKE, FAKE, 1, 2, 4, 2048, 1e-6, NUL) == gdn.GDN_EUNSUPPORTED
+    assert l2(FAKE_MIS, FAKE, 1, 2, 4, 32, 1e-6, NUL) == gdn.GDN_EALIGN
+    assert l2(NUL, NUL, 0, 2, 4, 32, 1e-6, NUL) == gdn.GDN_OK
+    nm = lib.gdn_gated_rmsnorm
+    assert nm(FAKE, NUL, FAKE, FAKE, 1, 32, 1e-6, NUL) == gdn.GDN_ENULL
+    assert nm(FAKE, FAKE, FAKE, FAKE, -1, 32, 1e-6, NUL) == gdn.GDN_ESIZE
+    assert nm(FAKE, FAKE, FAKE, FAKE, 1, 0, 1e-6, NUL) == gdn.GDN_ESIZE
+    assert nm(FAKE, FAKE, FAKE, FAKE, 1, 34, 1e-6, NUL) == gdn.GDN_EUNSUPPORTED
+    assert nm(FAKE, FAKE, FAKE_MIS, FAKE, 1, 32, 1e-6, NUL) == gdn.GDN_EALIGN
+    assert nm(NUL, NUL, NUL, NUL, 0, 32, 1e-6, NUL) == gdn.GDN_OK
+
+
+def test_block_validation(lib):
+    f = lib.gdn_decode_block_bf16
+
+    def call(first=FAKE, state=FAKE, n=1, HK=16, H=32, S=128, K=4, z=FAKE):
+        return f(first, z, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, state, FAKE,
+                 n, HK, H, S, K, 0.1, 1e-6, 1e-6, NUL)
+
+    assert call(first=NUL) == gdn.GDN_ENULL
+    assert call(n=-1) == gdn.GDN_ESIZE
+    assert call(HK=0) == gdn.GDN_ESIZE
+    assert call(HK=12) == gdn.GDN_ESIZE                 # 32 % 12 != 0
+    assert call(HK=4) == gdn.GDN_EUNSUPPORTED           # 8 V-heads per K-head
+    assert call(S=64) == gdn.GDN_EUNSUPPORTED
+    assert call(K=5) == gdn.GDN_EUNSUPPORTED
+    assert call(state=FAKE_MIS) == gdn.GDN_EALIGN
+    assert call(z=ctypes.c_void_p(0x10002)) == gdn.GDN_EALIGN
+    assert call(first=NUL, state=NUL, n=0) == gdn.GDN_OK
+
+
+def test_python_binding_rejects_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(4)
+    with pytest.raises(ValueError):
+        gdn.gdn_sigmoid(x, x)

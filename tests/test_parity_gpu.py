@@ -1,0 +1,410 @@
+"""Parity of the HIP library with the oracle, element by element, on the same
+seeded inputs (needs an MI355X).
+
+Covers each entry point at the five workloads' shapes (the full sizes of the
+batched decode and the 4096-token scan, and sampled layers of the 64-sequence
+bf16 block in the launch configuration the benchmark times), edge shapes
+(every supported state size, ragged token counts against the scan's 32-token
+chunks, several sequences, conv kernels 2..4 with fewer tokens than taps,
+zero vectors, extreme gate inputs, empty inputs), and the bit-level
+properties the pages state: a scan equals chained single steps, and the fused
+layer equals its stages chained.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (ATOL, DEV, RTOL, RTOL_LONG_SCAN, assert_close, dev, dev_bits, host,
+                         oracle_threads, prep_recurrence, widen_bf16)
+from linear_attention_ssm_recurrence_amd import gdn, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdn.load_library()
+    oracle_threads()
+
+
+def _rand_rec(rng, N, T, H, S, zero_state=False):
+    """Recurrence inputs drawn here (unit q, k; g <= 0; beta in (0,1)) via the oracle."""
+    q = oracle.l2norm_gqa(rng.standard_normal((N, T, H, S)), H)
+    k = oracle.l2norm_gqa(rng.standard_normal((N, T, H, S)), H)
+    v = rng.standard_normal((N, T, H, S)).astype(np.float32)
+    g = oracle.decay_gate(rng.standard_normal((N, T, H)), np.zeros(H), rng.standard_normal(H))
+    beta = oracle.sigmoid(rng.standard_normal((N, T, H)))
+    st = (np.zeros((N, H, S, S)) if zero_state else rng.standard_normal((N, H, S, S)) * 0.05)
+    return dict(q=q, k=k, v=v, g=g, beta=beta, state=st.astype(np.float32))
+
+
+def _gpu_scan(p, scale):
+    st = dev(p["state"])
+    y = torch.empty(p["v"].shape, dtype=torch.float32, device=DEV)
+    gdn.gdn_recurrence_seq(st, dev(p["q"]), dev(p["k"]), dev(p["v"]), dev(p["g"]), dev(p["beta"]),
+                           y, scale)
+    return y, st
+
+
+def _gpu_steps(p, scale):
+    """T chained decode launches."""
+    st = dev(p["state"])
+    N, T, H, S = p["v"].shape
+    q, k, v, g, b = (dev(p[x]) for x in ("q", "k", "v", "g", "beta"))
+    y = torch.empty((N, T, H, S), dtype=torch.float32, device=DEV)
+    for t in range(T):
+        yt = torch.empty((N, H, S), dtype=torch.float32, device=DEV)
+        gdn.gdn_recurrence(st, q[:, t].contiguous(), k[:, t].contiguous(), v[:, t].contiguous(),
+                           g[:, t].contiguous(), b[:, t].contiguous(), yt, scale)
+        y[:, t] = yt
+    return y, st
+
+
+# ---------------------------------------------------------------------------
+# Recurrence
+# ---------------------------------------------------------------------------
+
+def test_tiny_scan_config0():
+    """1 sequence, 2 heads, S = 32, 8 tokens, zero initial state."""
+    w = inputs.WORKLOADS[0]
+    p = prep_recurrence(inputs.draw(w), w)
+    y_ref, st_ref = oracle.recurrence_seq(p["state"], p["q"], p["k"], p["v"], p["g"], p["beta"], w.scale)
+    y, st = _gpu_scan(p, w.scale)
+    assert_close(host(y), y_ref, "tiny scan y")
+    assert_close(host(st), st_ref, "tiny scan state")
+    y2, st2 = _gpu_steps(p, w.scale)
+    assert torch.equal(y, y2) and torch.equal(st, st2), "scan != chained decode steps (bits)"
+
+
+@pytest.mark.parametrize("S", [32, 64, 128, 256])
+@pytest.mark.parametrize("N,T,H", [(1, 1, 1), (2, 33, 3), (1, 70, 2)])
+def test_scan_shapes(S, N, T, H):
+    rng = np.random.default_rng(1000 + S + 7 * T + N)
+    p = _rand_rec(rng, N, T, H, S)
+    scale = 1 / math.sqrt(S)
+    y_ref, st_ref = oracle.recurrence_seq(p["state"], p["q"], p["k"], p["v"], p["g"], p["beta"], scale)
+    y, st = _gpu_scan(p, scale)
+    assert_close(host(y), y_ref, f"scan y S={S} N={N} T={T} H={H}")
+    assert_close(host(st), st_ref, f"scan state S={S} N={N} T={T} H={H}")
+    if T <= 33:
+        y2, st2 = _gpu_steps(p, scale)
+        assert torch.equal(y, y2) and torch.equal(st, st2), "scan != chained decode steps (bits)"
+
+
+@pytest.mark.parametrize("S", [32, 64, 128, 256])
+@pytest.mark.parametrize("N,H", [(1, 1), (5, 3)])
+def test_decode_shapes(S, N, H):
+    rng = np.random.default_rng(2000 + S + N)
+    p = _rand_rec(rng, N, 1, H, S)
+    scale = 1 / math.sqrt(S)
+    y_ref, st_ref = oracle.recurrence_seq(p["state"], p["q"], p["k"], p["v"], p["g"], p["beta"], scale)
+    y, st = _gpu_steps(p, scale)
+    assert_close(host(y), y_ref, f"decode y S={S}")
+    assert_close(host(st), st_ref, f"decode state S={S}")
+
+
+def test_batched_decode_config2_full():
+    """256 sequences x 32 V-heads x S = 128 (512 MiB of state), every element."""
+    w = inputs.WORKLOADS[2]
+    d = inputs.draw(w)
+    p = prep_recurrence(d, w)
+    sq = lambda x: x[:, 0]
+    y_ref, st_ref = oracle.recurrence(p["state"], sq(p["q"]), sq(p["k"]), sq(p["v"]),
+                                      sq(p["g"]), sq(p["beta"]), w.scale)
+    st = dev(p["state"])
+    y = torch.empty((w.n_seqs, w.n_v_heads, w.state_size), dtype=torch.float32, device=DEV)
+    q, k, v, g, b = (dev(sq(p[x])) for x in ("q", "k", "v", "g", "beta"))
+    gdn.gdn_recurrence(st, q, k, v, g, b, y, w.scale)
+    assert_close(host(y), y_ref, "config2 y")
+    assert_close(host(st), st_ref, "config2 state")
+    # same launch again from the same state: identical bits
+    st2 = dev(p["state"])
+    y2 = torch.empty_like(y)
+    gdn.gdn_recurrence(st2, q, k, v, g, b, y2, w.scale)
+    assert torch.equal(st, st2) and torch.equal(y, y2), "decode is not deterministic"
+
+
+def test_scan_config3_full():
+    """1 sequence, 4096 tokens, 32 heads, S = 128, zero initial state; the final
+    state must also equal 4096 chained decode launches."""
+    w = inputs.WORKLOADS[3]
+    d = inputs.draw(w, with_conv=False)
+    p = prep_recurrence(d, w)
+    y_ref, st_ref = oracle.recurrence_seq(p["state"], p["q"], p["k"], p["v"], p["g"], p["beta"], w.scale)
+    y, st = _gpu_scan(p, w.scale)
+    assert_close(host(y), y_ref, "config3 y", rtol=RTOL_LONG_SCAN)
+    assert_close(host(st), st_ref, "config3 final state", rtol=RTOL_LONG_SCAN)
+    y2, st2 = _gpu_steps(p, w.scale)
+    assert torch.equal(st, st2), "4096-token scan != 4096 chained decode launches (state bits)"
+    assert torch.equal(y, y2), "4096-token scan != 4096 chained decode launches (y bits)"
+
+
+def test_scan_split_resume():
+    rng = np.random.default_rng(77)
+    p = _rand_rec(rng, 2, 50, 2, 128)
+    y, st = _gpu_scan(p, 0.1)
+    a = {k: (v[:, :20] if v.ndim >= 3 and k != "state" else v) for k, v in p.items()}
+    y1, st1 = _gpu_scan(a, 0.1)
+    b = {k: (v[:, 20:] if v.ndim >= 3 and k != "state" else v) for k, v in p.items()}
+    b["state"] = host(st1)
+    y2, st2 = _gpu_scan(b, 0.1)
+    assert torch.equal(torch.cat([y1, y2], dim=1), y) and torch.equal(st2, st)
+
+
+# ---------------------------------------------------------------------------
+# Conv1d + SiLU
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("K", [2, 3, 4])
+@pytest.mark.parametrize("N,T,C", [(1, 1, 5), (2, 2, 300), (1, 3, 257), (2, 40, 64)])
+def test_conv_shapes(K, N, T, C):
+    rng = np.random.default_rng(3000 + 10 * K + T)
+    x = rng.standard_normal((N, T, C)).astype(np.float32)
+    w = (rng.standard_normal((C, K)) * 0.5).astype(np.float32)
+    cs0 = rng.standard_normal((N, C, K - 1)).astype(np.float32)
+    out_ref, cs_ref = oracle.conv1d_silu_seq(x, w, cs0)
+    cs = dev(cs0)
+    out = torch.empty((N, T, C), dtype=torch.float32, device=DEV)
+    gdn.gdn_conv1d_silu_seq(dev(x), dev(w), cs, out)
+    assert_close(host(out), out_ref, f"conv seq out K={K} T={T}")
+    assert np.array_equal(host(cs), cs_ref), f"conv history K={K} T={T}"
+    # single steps give the same bits
+    cs2 = dev(cs0)
+    xs = dev(x)
+    for t in range(T):
+        o = torch.empty((N, C), dtype=torch.float32, device=DEV)
+        gdn.gdn_conv1d_silu(xs[:, t].contiguous(), dev(w), cs2, o)
+        assert torch.equal(o, out[:, t]), f"conv step {t} != scan"
+    assert torch.equal(cs2, cs)
+
+
+def test_conv_config3_full():
+    """x [4096][8192] ~ N(0,1), w ~ N(0, 0.5), zero history."""
+    w = inputs.WORKLOADS[3]
+    d = inputs.draw(w)
+    out_ref, cs_ref = oracle.conv1d_silu_seq(d["x"], d["conv_w"], d["conv_state"])
+    cs = dev(d["conv_state"])
+    out = torch.empty(d["x"].shape, dtype=torch.float32, device=DEV)
+    gdn.gdn_conv1d_silu_seq(dev(d["x"]), dev(d["conv_w"]), cs, out)
+    assert_close(host(out), out_ref, "config3 conv out")
+    assert np.array_equal(host(cs), cs_ref), "config3 conv history"
+
+
+# ---------------------------------------------------------------------------
+# Companions
+# ---------------------------------------------------------------------------
+
+def test_decay_gate_and_sigmoid():
+    rng = np.random.default_rng(41)
+    H = 32
+    a = (rng.standard_normal((97, H)) * 6).astype(np.float32)
+    a[0, :8] = [25.0, 1e4, 1e30, -80.0, 19.999, 20.0, 20.001, 0.0]
+    dt = (rng.standard_normal(H) * 0.5).astype(np.float32)
+    A_log = rng.standard_normal(H).astype(np.float32)
+    g = torch.empty((97, H), dtype=torch.float32, device=DEV)
+    gdn.gdn_decay_gate(dev(a), dev(dt), dev(A_log), g)
+    gh = host(g)
+    assert (gh <= 0).all() and np.isfinite(gh).all()
+    assert_close(gh, oracle.decay_gate(a, dt, A_log), "decay gate")
+    x = (rng.standard_normal(1001) * 10).astype(np.float32)
+    y = torch.empty(1001, dtype=torch.float32, device=DEV)
+    gdn.gdn_sigmoid(dev(x), y)
+    assert_close(host(y), oracle.sigmoid(x), "sigmoid")
+    xd = dev(x)
+    gdn.gdn_sigmoid(xd, xd)   # in place
+    assert torch.equal(xd, y)
+
+
+@pytest.mark.parametrize("HK,H,D", [(16, 32, 128), (2, 2, 32), (3, 12, 96), (1, 4, 1024)])
+def test_l2norm_gqa(HK, H, D):
+    rng = np.random.default_rng(HK * 100 + D)
+    x = rng.standard_normal((5, HK, D)).astype(np.float32)
+    x[0, 0] = 0.0                     # zero vector -> divided by eps -> zeros
+    x[1, 0] = 1e-9                    # shorter than eps
+    out = torch.empty((5, H, D), dtype=torch.float32, device=DEV)
+    gdn.gdn_l2norm_gqa(dev(x), out, 1e-6)
+    ref = oracle.l2norm_gqa(x, H, 1e-6)
+    assert_close(host(out), ref, f"l2norm HK={HK} H={H} D={D}")
+    o = host(out)
+    for vh in range(H):
+        assert np.array_equal(o[:, vh], o[:, vh % HK])
+
+
+@pytest.mark.parametrize("D", [32, 96, 128, 260, 1024])
+def test_gated_rmsnorm(D):
+    rng = np.random.default_rng(D)
+    y = rng.standard_normal((37, D)).astype(np.float32)
+    y[3] = 0.0
+    z = (rng.standard_normal((37, D)) * 3).astype(np.float32)
+    w = (1 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    out = torch.empty((37, D), dtype=torch.float32, device=DEV)
+    gdn.gdn_gated_rmsnorm(dev(y), dev(w), dev(z), out, 1e-6)
+    assert_close(host(out), oracle.gated_rmsnorm(y, w, z, 1e-6), f"gated norm D={D}")
+
+
+def test_single_decode_config1_stages_and_chain():
+    """Every stage at the single-decode shapes (16 -> 32 heads, S = 128,
+    C = 8192), then the fp32 decode layer chained on the GPU against the
+    chained oracle."""
+    w = inputs.WORKLOADS[1]
+    d = inputs.draw(w)
+    H, HK, S = w.n_v_heads, w.n_k_heads, w.state_size
+    p = prep_recurrence(d, w)
+    # stage by stage
+    qg = torch.empty((1, 1, H, S), dtype=torch.float32, device=DEV)
+    gdn.gdn_l2norm_gqa(dev(d["q_raw"]), qg, w.l2_eps)
+    assert_close(host(qg), p["q"], "config1 q l2norm+gqa")
+    g = torch.empty((1, 1, H), dtype=torch.float32, device=DEV)
+    gdn.gdn_decay_gate(dev(d["a"]), dev(d["dt_bias"]), dev(d["A_log"]), g)
+    assert_close(host(g), p["g"], "config1 gate")
+    bt = torch.empty((1, 1, H), dtype=torch.float32, device=DEV)
+    gdn.gdn_sigmoid(dev(d["b"]), bt)
+    assert_close(host(bt), p["beta"], "config1 beta")
+    y_ref, st_ref = oracle.recurrence(p["state"], p["q"][:, 0], p["k"][:, 0], p["v"][:, 0],
+                                      p["g"][:, 0], p["beta"][:, 0], w.scale)
+    st = dev(p["state"])
+    y = torch.empty((1, H, S), dtype=torch.float32, device=DEV)
+    gdn.gdn_recurrence(st, dev(p["q"][:, 0]), dev(p["k"][:, 0]), dev(p["v"][:, 0]),
+                       dev(p["g"][:, 0]), dev(p["beta"][:, 0]), y, w.scale)
+    assert_close(host(y), y_ref, "config1 y")
+    assert_close(host(st), st_ref, "config1 state")
+    out = torch.empty((1, H, S), dtype=torch.float32, device=DEV)
+    gdn.gdn_gated_rmsnorm(y, dev(d["norm_w"]), dev(d["z"][:, 0]), out, w.eps)
+    assert_close(host(out), oracle.gated_rmsnorm(host(y), d["norm_w"], d["z"][:, 0], w.eps), "config1 norm")
+    co_ref, cs_ref = oracle.conv1d_silu(d["x"][:, 0], d["conv_w"], d["conv_state"])
+    cs = dev(d["conv_state"])
+    co = torch.empty((1, w.conv_dim), dtype=torch.float32, device=DEV)
+    gdn.gdn_conv1d_silu(dev(d["x"][:, 0]), dev(d["conv_w"]), cs, co)
+    assert_close(host(co), co_ref, "config1 conv")
+    assert np.array_equal(host(cs), cs_ref)
+
+    # chained: conv -> split -> l2norm + gqa -> gate, beta -> recurrence -> norm
+    kd = HK * S
+    co_np = co_ref
+    qn = oracle.l2norm_gqa(co_np[:, :kd].reshape(1, HK, S), H, w.l2_eps)
+    kn = oracle.l2norm_gqa(co_np[:, kd:2 * kd].reshape(1, HK, S), H, w.l2_eps)
+    vv = co_np[:, 2 * kd:].reshape(1, H, S)
+    gg = oracle.decay_gate(d["a"][:, 0], d["dt_bias"], d["A_log"])
+    bb = oracle.sigmoid(d["b"][:, 0])
+    yc_ref, stc_ref = oracle.recurrence(d["state"], qn, kn, vv, gg, bb, w.scale)
+    oc_ref = oracle.gated_rmsnorm(yc_ref, d["norm_w"], d["z"][:, 0], w.eps)
+
+    qd = torch.empty((1, H, S), dtype=torch.float32, device=DEV)
+    kdv = torch.empty((1, H, S), dtype=torch.float32, device=DEV)
+    gdn.gdn_l2norm_gqa(co[:, :kd].reshape(1, HK, S).contiguous(), qd, w.l2_eps)
+    gdn.gdn_l2norm_gqa(co[:, kd:2 * kd].reshape(1, HK, S).contiguous(), kdv, w.l2_eps)
+    gdd = torch.empty((1, H), dtype=torch.float32, device=DEV)
+    bdd = torch.empty((1, H), dtype=torch.float32, device=DEV)
+    gdn.gdn_decay_gate(dev(d["a"][:, 0]), dev(d["dt_bias"]), dev(d["A_log"]), gdd)
+    gdn.gdn_sigmoid(dev(d["b"][:, 0]), bdd)
+    stc = dev(d["state"])
+    yc = torch.empty((1, H, S), dtype=torch.float32, device=DEV)
+    gdn.gdn_recurrence(stc, qd, kdv, co[:, 2 * kd:].reshape(1, H, S).contiguous(), gdd, bdd, yc, w.scale)
+    oc = torch.empty((1, H, S), dtype=torch.float32, device=DEV)
+    gdn.gdn_gated_rmsnorm(yc, dev(d["norm_w"]), dev(d["z"][:, 0]), oc, w.eps)
+    assert_close(host(yc), yc_ref, "config1 chained y")
+    assert_close(host(stc), stc_ref, "config1 chained state")
+    assert_close(host(oc), oc_ref, "config1 chained out")
+
+
+# ---------------------------------------------------------------------------
+# Fused bf16 decode layer
+# ---------------------------------------------------------------------------
+
+def _block_gpu(d, HK, scale, eps=1e-6):
+    N, H, S = d["z"].shape
+    cs, st = dev(d["conv_state"]), dev(d["state"])
+    out = torch.empty((N, H, S), dtype=torch.float32, device=DEV)
+    gdn.gdn_decode_block_bf16(dev_bits(d["qkv"]), dev_bits(d["z"]), dev(d["a"]), dev(d["b"]),
+                              dev(d["conv_w"]), dev(d["A_log"]), dev(d["dt_bias"]),
+                              dev(d["norm_w"]), cs, st, out, HK, scale, eps, eps)
+    return out, cs, st
+
+
+def _block_staged_gpu(d, HK, scale, eps=1e-6):
+    """The same layer through the stand-alone kernels."""
+    N, H, S = d["z"].shape
+    C, K = d["conv_w"].shape
+    kd = HK * S
+    cs, st = dev(d["conv_state"]), dev(d["state"])
+    co = torch.empty((N, C), dtype=torch.float32, device=DEV)
+    gdn.gdn_conv1d_silu(widen_bf16(dev_bits(d["qkv"])).contiguous(), dev(d["conv_w"]), cs, co)
+    q = torch.empty((N, H, S), dtype=torch.float32, device=DEV)
+    k = torch.empty((N, H, S), dtype=torch.float32, device=DEV)
+    gdn.gdn_l2norm_gqa(co[:, :kd].reshape(N, HK, S).contiguous(), q, eps)
+    gdn.gdn_l2norm_gqa(co[:, kd:2 * kd].reshape(N, HK, S).contiguous(), k, eps)
+    g = torch.empty((N, H), dtype=torch.float32, device=DEV)
+    b = torch.empty((N, H), dtype=torch.float32, device=DEV)
+    gdn.gdn_decay_gate(dev(d["a"]), dev(d["dt_bias"]), dev(d["A_log"]), g)
+    gdn.gdn_sigmoid(dev(d["b"]), b)
+    y = torch.empty((N, H, S), dtype=torch.float32, device=DEV)
+    gdn.gdn_recurrence(st, q, k, co[:, 2 * kd:].reshape(N, H, S).contiguous(), g, b, y, scale)
+    out = torch.empty((N, H, S), dtype=torch.float32, device=DEV)
+    gdn.gdn_gated_rmsnorm(y, dev(d["norm_w"]), widen_bf16(dev_bits(d["z"])).contiguous(), out, eps)
+    return out, cs, st
+
+
+def _check_block(d, HK, scale, what):
+    out, cs, st = _block_gpu(d, HK, scale)
+    o_ref, cs_ref, st_ref = oracle.decode_block_bf16(
+        d["qkv"], d["z"], d["a"], d["b"], d["conv_w"], d["A_log"], d["dt_bias"], d["norm_w"],
+        d["conv_state"], d["state"], HK, scale, 1e-6, 1e-6)
+    assert_close(host(out), o_ref, f"{what} out")
+    assert_close(host(st), st_ref, f"{what} state")
+    assert np.array_equal(host(cs), cs_ref), f"{what} conv history"
+    out2, cs2, st2 = _block_staged_gpu(d, HK, scale)
+    assert torch.equal(out, out2), f"{what}: fused layer != staged kernels (out bits)"
+    assert torch.equal(st, st2), f"{what}: fused layer != staged kernels (state bits)"
+    assert torch.equal(cs, cs2), f"{what}: fused layer != staged kernels (history bits)"
+
+
+@pytest.mark.parametrize("layer", [0, 47])
+def test_block_config4_layers(layer):
+    """64 sequences, 16 K-heads -> 32 V-heads, S = 128, C = 8192, K = 4: one
+    launch per layer, as the benchmark runs it."""
+    w = inputs.WORKLOADS[4]
+    d = inputs.draw_block_layer(layer)
+    _check_block(d, w.n_k_heads, w.scale, f"config4 layer {layer}")
+
+
+@pytest.mark.parametrize("GQ", [1, 2, 4])
+@pytest.mark.parametrize("K", [2, 3, 4])
+def test_block_shapes(GQ, K):
+    rng = np.random.default_rng(GQ * 10 + K)
+    N, HK, S = 3, 2, 128
+    H = GQ * HK
+    C = 2 * HK * S + H * S
+    bits = lambda x: inputs.to_bf16_bits(x.astype(np.float32))
+    d = dict(qkv=bits(rng.standard_normal((N, C))), z=bits(rng.standard_normal((N, H, S))),
+             a=rng.standard_normal((N, H)).astype(np.float32),
+             b=rng.standard_normal((N, H)).astype(np.float32),
+             conv_w=(rng.standard_normal((C, K)) * 0.5).astype(np.float32),
+             A_log=rng.standard_normal(H).astype(np.float32),
+             dt_bias=(0.1 * rng.standard_normal(H)).astype(np.float32),
+             norm_w=(1 + 0.1 * rng.standard_normal(S)).astype(np.float32),
+             conv_state=rng.standard_normal((N, C, K - 1)).astype(np.float32),
+             state=(0.05 * rng.standard_normal((N, H, S, S))).astype(np.float32))
+    _check_block(d, HK, 1 / math.sqrt(S), f"block GQ={GQ} K={K}")
+
+
+# ---------------------------------------------------------------------------
+# Empty inputs
+# ---------------------------------------------------------------------------
+
+def test_empty_inputs_are_noops():
+    e = lambda *s: torch.empty(s, dtype=torch.float32, device=DEV)
+    gdn.gdn_recurrence(e(0, 4, 32, 32), e(0, 4, 32), e(0, 4, 32), e(0, 4, 32), e(0, 4), e(0, 4),
+                       e(0, 4, 32), 0.1)
+    st = torch.ones((1, 2, 32, 32), device=DEV)
+    gdn.gdn_recurrence_seq(st, e(1, 0, 2, 32), e(1, 0, 2, 32), e(1, 0, 2, 32), e(1, 0, 2),
+                           e(1, 0, 2), e(1, 0, 2, 32), 0.1)
+    cs = torch.ones((2, 8, 3), device=DEV)
+    gdn.gdn_conv1d_silu_seq(e(2, 0, 8), e(8, 4), cs, e(2, 0, 8))
+    gdn.gdn_gated_rmsnorm(e(0, 32), e(32), e(0, 32), e(0, 32))
+    torch.cuda.synchronize()
+    assert torch.equal(st, torch.ones_like(st)) and torch.equal(cs, torch.ones_like(cs))
