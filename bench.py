@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 512 MiB device copy three times (a known-size "
+                         "kernel for scaling hardware byte counters)")
     return ap.parse_args()
 
 
@@ -291,6 +294,30 @@ def run_block(torch, gdn, inputs, steps, warmup):
     }
 
 
+DECODE_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "recurrence_decode_256x32x128_traffic.md")
+DECODE_SOURCES = ("linear_attention_ssm_recurrence_amd/csrc/gdn_recurrence.hip",
+                  "linear_attention_ssm_recurrence_amd/csrc/gdn_device.hpp")
+
+
+def recorded_traffic():
+    """HBM bytes per decode launch from the committed counter summary, or None
+    when the kernel sources changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(DECODE_TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines()
+                  if line.startswith(("traffic_bytes_per_launch: ", "source_sha256: ")))
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("source_sha256", "").strip() != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(inputs, d, budget_s):
     """The C oracle's decode recurrence on a sample of the headline batch, on
     this host's cores. The oracle routine is called directly on arrays
@@ -368,6 +395,18 @@ def main():
         out_legs["block"] = run_block(torch, gdn, inputs, K, W)
         torch.cuda.empty_cache()
 
+    if args.calibrate_copy:
+        log("copy calibration: 3 x 512 MiB device-to-device copy")
+        src = torch.ones(128 * 1024 * 1024, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        with Timer(torch) as tc:
+            for _ in range(3):
+                dst.copy_(src)
+        line_copy = {"bytes_read_per_copy": src.numel() * 4, "bytes_written_per_copy": src.numel() * 4,
+                     "GBps": 2 * src.numel() * 4 * 3 / (tc.event_ms * 1e-3) / 1e9}
+        del src, dst
     achieved = dec["algorithmic_bytes_per_launch"] / (dec["kernel_ms_events"] * 1e-3) / 1e9
     line = {
         "metric": METRIC,
@@ -392,9 +431,11 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS,
                      "kernel_ms": dec["kernel_ms_events"],
                      "bytes_per_launch": dec["algorithmic_bytes_per_launch"],
-                     "traffic": None},
+                     "traffic": recorded_traffic()},
         "legs": out_legs,
     }
+    if args.calibrate_copy:
+        line["copy_calibration"] = line_copy
     if "scan" in out_legs:
         line["scan_tokens_per_s"] = out_legs["scan"]["tokens_per_s"]
     if not args.no_cpu_baseline:
