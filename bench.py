@@ -426,7 +426,7 @@ def main():
                    "n_k_heads": w.n_k_heads, "state_size": w.state_size,
                    "state_bytes_per_step": dec["state_bytes_per_launch"]},
         "frac_hbm_peak_state": dec["state_GBps"] / HBM_PEAK_GBS,
-        "roofline": {"bound": "hbm", "kernel": "recurrence_decode_kernel<128,32>",
+        "roofline": {"bound": "hbm", "kernel": "recurrence_decode_kernel<128,8>",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "kernel_ms": dec["kernel_ms_events"],

@@ -22,12 +22,18 @@ namespace gdn {
 // ---------------------------------------------------------------------------
 // Decode: each wave owns RW consecutive rows of one (sequence, head). It
 // issues every state load of its rows first (RW/G * E/4 float4 loads per
-// lane, all independent), then runs the step row-group by row-group and
-// streams the rows back. k and q of the head are loaded once per wave and
-// reused for all its rows; g and beta are wave-uniform.
+// lane, all independent, non-temporal: the state is touched once per launch),
+// then runs the step row-group by row-group and streams the rows back with
+// non-temporal stores. k and q of the head are loaded once per wave and reused
+// for all its rows; g and beta are wave-uniform. Small waves (8 rows, 4 KiB of
+// state) in 8-wave blocks keep the most requests in flight across the chip:
+// measured on MI355X at S = 128 this streams faster than 16- or 32-row waves
+// and than a plain non-temporal copy kernel.
 // ---------------------------------------------------------------------------
+constexpr int kDecodeWaves = 8;
+
 template <int S, int RW>
-__global__ __launch_bounds__(256) void recurrence_decode_kernel(
+__global__ __launch_bounds__(64 * kDecodeWaves) void recurrence_decode_kernel(
     float* __restrict__ state, const float* __restrict__ q, const float* __restrict__ k,
     const float* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
     float* __restrict__ y, int64_t n_pairs, float scale) {
@@ -76,20 +82,19 @@ __global__ __launch_bounds__(256) void recurrence_decode_kernel(
 
 template <int S>
 struct DecodeCfg;
-template <> struct DecodeCfg<32> { static constexpr int RW = 32; };
-template <> struct DecodeCfg<64> { static constexpr int RW = 32; };
-template <> struct DecodeCfg<128> { static constexpr int RW = 32; };
-template <> struct DecodeCfg<256> { static constexpr int RW = 16; };
+template <> struct DecodeCfg<32> { static constexpr int RW = 16; };   // G = 16 rows per slot
+template <> struct DecodeCfg<64> { static constexpr int RW = 8; };
+template <> struct DecodeCfg<128> { static constexpr int RW = 8; };
+template <> struct DecodeCfg<256> { static constexpr int RW = 8; };
 
 template <int S>
 static int launch_decode(float* state, const float* q, const float* k, const float* v,
                          const float* g, const float* beta, float* y, int64_t n_pairs,
                          float scale, hipStream_t stream) {
   constexpr int RW = DecodeCfg<S>::RW;
-  constexpr int WAVES_PER_BLOCK = 4;
   const int64_t waves = n_pairs * (S / RW);
-  const unsigned blocks = grid_for(waves, WAVES_PER_BLOCK);
-  hipLaunchKernelGGL((recurrence_decode_kernel<S, RW>), dim3(blocks), dim3(64 * WAVES_PER_BLOCK),
+  const unsigned blocks = grid_for(waves, kDecodeWaves);
+  hipLaunchKernelGGL((recurrence_decode_kernel<S, RW>), dim3(blocks), dim3(64 * kDecodeWaves),
                      0, stream, state, q, k, v, g, beta, y, n_pairs, scale);
   return launch_status();
 }
@@ -97,11 +102,19 @@ static int launch_decode(float* state, const float* q, const float* k, const flo
 // ---------------------------------------------------------------------------
 // Scan: a block of W waves owns R = W*G consecutive rows of one (sequence,
 // head) and carries them in VGPRs through all tokens. Per chunk of CT tokens
+// (64; 16 at S = 256, where LDS is the limit)
 // the block stages k and q of its head, v of its rows, and exp(g) and beta
 // into LDS; the next chunk's global loads are issued before the current chunk
 // is computed and land in the other LDS buffer, so there is one barrier per
 // chunk and none per token. exp(g) is evaluated once per token per block (by
-// the staging thread), not once per lane.
+// the staging thread), not once per lane. A full chunk is unrolled, so every
+// LDS read has an immediate offset and the next token's reads are scheduled
+// under the current token's arithmetic; y goes to its own LDS array (which
+// no read of the chunk can alias) and is written to HBM once per chunk.
+//
+// Block order: the BPH blocks of one head read the same k and q, so they are
+// numbered to land on the same XCD (the hardware deals consecutive block ids
+// round-robin over the 8 XCDs) and share that XCD's L2.
 // ---------------------------------------------------------------------------
 template <int S>
 struct ScanCfg {
@@ -109,11 +122,14 @@ struct ScanCfg {
   static constexpr int W = (S / Lay::G) < 4 ? (S / Lay::G) : 4;  // waves per block
   static constexpr int R = W * Lay::G;                            // rows per block
   static constexpr int BPH = S / R;                               // blocks per head
-  static constexpr int CT = S >= 256 ? 16 : 32;                   // tokens per chunk
+  static constexpr int CT = S >= 256 ? 16 : 64;                   // tokens per chunk
   static constexpr int THREADS = 64 * W;
   // LDS words of one chunk buffer: k, q [CT][S], v [CT][R], decay, beta [CT]
   static constexpr int KQ = CT * S;
-  static constexpr int BUF = 2 * KQ + CT * R + 2 * CT;
+  static constexpr int VOFF = 2 * KQ;
+  static constexpr int DOFF = VOFF + CT * R;
+  static constexpr int BOFF = DOFF + CT;
+  static constexpr int BUF = BOFF + CT;
   // float4 loads of k and q per thread per chunk (each of k and q)
   static constexpr int KQ4 = KQ / 4 / THREADS;
   static constexpr int VPT = (CT * R + THREADS - 1) / THREADS;    // v loads per thread
@@ -121,8 +137,17 @@ struct ScanCfg {
   static_assert(CT <= THREADS, "one staging thread per token");
 };
 
+constexpr int kXcds = 8;
+
+// Block id -> logical block, so that logical blocks b and b+1 share an XCD.
+__device__ __forceinline__ unsigned xcd_group(unsigned bid, unsigned nblocks) {
+  if (nblocks % kXcds != 0) return bid;
+  return (bid % kXcds) * (nblocks / kXcds) + bid / kXcds;
+}
+
 template <int S>
-__global__ __launch_bounds__(ScanCfg<S>::THREADS) void recurrence_scan_kernel(
+__global__ __launch_bounds__(ScanCfg<S>::THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void recurrence_scan_kernel(
     float* __restrict__ state, const float* __restrict__ q, const float* __restrict__ k,
     const float* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
     float* __restrict__ y, int n_tokens, int n_v_heads, float scale) {
@@ -131,13 +156,15 @@ __global__ __launch_bounds__(ScanCfg<S>::THREADS) void recurrence_scan_kernel(
   constexpr int E = Lay::E, L = Lay::L, G = Lay::G;
   constexpr int CT = Cfg::CT, R = Cfg::R, KQ = Cfg::KQ, BUF = Cfg::BUF, THREADS = Cfg::THREADS;
   __shared__ float smem[2 * BUF];
+  __shared__ float ysm[CT * R];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
   const int p = lane % L;
-  const int64_t head = blockIdx.x / Cfg::BPH;          // n * H + h
-  const int rblk = (int)(blockIdx.x % Cfg::BPH) * R;    // first row of the block
+  const unsigned blk = xcd_group(blockIdx.x, gridDim.x);
+  const int64_t head = blk / Cfg::BPH;                 // n * H + h
+  const int rblk = (int)(blk % Cfg::BPH) * R;           // first row of the block
   const int64_t n = head / n_v_heads;
   const int h = (int)(head % n_v_heads);
   const int lrow = wv * G + lane / L;                   // row within the block
@@ -148,7 +175,7 @@ __global__ __launch_bounds__(ScanCfg<S>::THREADS) void recurrence_scan_kernel(
   const float* qn = q + base_n * tok_stride + (int64_t)h * S;
   const float* kn = k + base_n * tok_stride + (int64_t)h * S;
   const float* vn = v + base_n * tok_stride + (int64_t)h * S + rblk;
-  float* yn = y + base_n * tok_stride + (int64_t)h * S + row;
+  float* yn = y + base_n * tok_stride + (int64_t)h * S + rblk;
   const float* gn = g + base_n * n_v_heads + h;
   const float* bn = beta + base_n * n_v_heads + h;
 
@@ -192,17 +219,48 @@ __global__ __launch_bounds__(ScanCfg<S>::THREADS) void recurrence_scan_kernel(
 #pragma unroll
     for (int i = 0; i < Cfg::VPT; ++i) {
       const int f = i * THREADS + tid;
-      if (f < CT * R && f / R < ct) buf[2 * KQ + f] = pv[i];
+      if (f < CT * R && f / R < ct) buf[Cfg::VOFF + f] = pv[i];
     }
     if (tid < ct) {
-      buf[2 * KQ + CT * R + tid] = pdec;
-      buf[2 * KQ + CT * R + CT + tid] = pbeta;
+      buf[Cfg::DOFF + tid] = pdec;
+      buf[Cfg::BOFF + tid] = pbeta;
     }
   };
 
   float r[E];
   float* srow = state + head * (int64_t)S * S + (int64_t)row * S;
   load_row_part<E, L>(srow, p, r);
+
+  // One token of the chunk in buffer `buf`; y goes to ysm (every lane of the
+  // row writes the same value).
+  auto token = [&](const float* buf, int tt) {
+    float kk[E], qq[E];
+    load_row_part<E, L>(buf + tt * S, p, kk);
+    load_row_part<E, L>(buf + KQ + tt * S, p, qq);
+    const float vj = buf[Cfg::VOFF + tt * R + lrow];
+    const float d = buf[Cfg::DOFF + tt];
+    const float b = buf[Cfg::BOFF + tt];
+    ysm[tt * R + lrow] = delta_rule_step<E, L>(r, kk, qq, vj, d, b, scale);
+  };
+  // A full chunk with the next token's LDS reads issued before the current
+  // token's arithmetic (two register sets, rotated by the unrolled loop).
+  auto full_chunk = [&](const float* buf) {
+    float kk[2][E], qq[2][E], vj[2], d[2], b[2];
+    auto read = [&](int tt, int slot) {
+      load_row_part<E, L>(buf + tt * S, p, kk[slot]);
+      load_row_part<E, L>(buf + KQ + tt * S, p, qq[slot]);
+      vj[slot] = buf[Cfg::VOFF + tt * R + lrow];
+      d[slot] = buf[Cfg::DOFF + tt];
+      b[slot] = buf[Cfg::BOFF + tt];
+    };
+    read(0, 0);
+#pragma unroll
+    for (int tt = 0; tt < CT; ++tt) {
+      const int cur = tt & 1;
+      if (tt + 1 < CT) read(tt + 1, cur ^ 1);
+      ysm[tt * R + lrow] = delta_rule_step<E, L>(r, kk[cur], qq[cur], vj[cur], d[cur], b[cur], scale);
+    }
+  };
 
   fetch(0);
   deposit(smem, 0);
@@ -214,17 +272,18 @@ __global__ __launch_bounds__(ScanCfg<S>::THREADS) void recurrence_scan_kernel(
     const bool more = t0 + CT < n_tokens;
     if (more) fetch(t0 + CT);
     const float* buf = smem + buf_id * BUF;
-    for (int tt = 0; tt < ct; ++tt) {
-      float kk[E], qq[E];
-      load_row_part<E, L>(buf + tt * S, p, kk);
-      load_row_part<E, L>(buf + KQ + tt * S, p, qq);
-      const float vj = buf[2 * KQ + tt * R + lrow];
-      const float d = buf[2 * KQ + CT * R + tt];
-      const float b = buf[2 * KQ + CT * R + CT + tt];
-      const float yj = delta_rule_step<E, L>(r, kk, qq, vj, d, b, scale);
-      if (p == 0) yn[(int64_t)(t0 + tt) * tok_stride] = yj;
+    if (ct == CT) {
+      full_chunk(buf);
+    } else {
+      for (int tt = 0; tt < ct; ++tt) token(buf, tt);
     }
     if (more) deposit(smem + (buf_id ^ 1) * BUF, t0 + CT);
+    __syncthreads();
+    // y of this chunk: R contiguous floats per token
+    for (int i = tid; i < ct * R; i += THREADS) {
+      const int tt = i / R, rr = i % R;
+      yn[(int64_t)(t0 + tt) * tok_stride + rr] = ysm[i];
+    }
     __syncthreads();
     buf_id ^= 1;
   }
@@ -256,7 +315,7 @@ static int check_recurrence(float* state, const float* q, const float* k, const 
   if (!mul_ok(n_seqs, n_v_heads, &pairs) || !mul_ok(pairs, (int64_t)state_size * state_size, &st) ||
       !mul_ok(pairs * n_tokens, state_size, &vec))
     return GDN_ESIZE;
-  if (pairs * (state_size / 16) >= (int64_t(1) << 31)) return GDN_ESIZE;  // grid limit
+  if (pairs * (state_size / 8) / kDecodeWaves >= (int64_t(1) << 31)) return GDN_ESIZE;  // grid limit
   if (!aligned16(state) || !aligned16(q) || !aligned16(k)) return GDN_EALIGN;
   return GDN_OK;
 }
