@@ -17,6 +17,10 @@ The same line carries the other workloads of the hot path ("legs"):
   decode_full the headline batch with its per-token glue launched too
               (decay gate, sigmoid, L2 norm + GQA of q and k) before the
               recurrence
+  decode_t4   the headline batch with the "T4" read-out (gdn_recurrence_ex)
+  spec        a speculative-decoding verify step: 64 sequences x 4 draft
+              tokens, 16 -> 32 heads by index, S = 128, conv over C = 8192,
+              with per-token state and conv snapshots
 and the roofline of the dominant kernel (the decode recurrence) measured with
 HIP events on the stream it runs on, and the CPU oracle timed on this host.
 
@@ -56,7 +60,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="decode,scan,block,decode_full")
+    ap.add_argument("--legs", default="decode,scan,block,decode_full,decode_t4,spec")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
@@ -148,14 +152,18 @@ def decode_bytes(w) -> dict:
     return {"state": state, "total": state + vecs + scal}
 
 
-def run_decode(torch, gdn, inputs, steps, warmup, with_glue=False):
+def run_decode(torch, gdn, inputs, steps, warmup, with_glue=False, t4=False):
     w, d, t = decode_inputs(torch, gdn, inputs)
 
     def step(i):
         if with_glue:
             t["glue"]()
-        gdn.gdn_recurrence(t["states"][i % 2], t["q"], t["k"], t["v"], t["g"], t["beta"],
-                           t["y"], w.scale)
+        if t4:
+            gdn.gdn_recurrence_ex(t["states"][i % 2], t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                  t["y"], w.scale, gdn.GDN_RECUR_T4)
+        else:
+            gdn.gdn_recurrence(t["states"][i % 2], t["q"], t["k"], t["v"], t["g"], t["beta"],
+                               t["y"], w.scale)
 
     for i in range(warmup):
         step(i)
@@ -238,6 +246,48 @@ def run_scan(torch, gdn, inputs, steps, warmup):
         "conv_GBps": conv_bytes / (conv_ms * 1e-3) / 1e9,
         "conv_frac_hbm_peak": conv_bytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
     }
+
+
+def run_spec(torch, gdn, inputs, steps, warmup):
+    """Verify step of speculative decoding: T draft tokens of N sequences
+    through conv (with history snapshots) and the scan (with state
+    snapshots), q/k repeated to the V-heads by index."""
+    N, T, HK, H, S, C, K = 64, 4, 16, 32, 128, 8192, 4
+    w = inputs.Workload(5, "spec", N, T, H, HK, S, conv_dim=C, state_sigma=0.05,
+                        conv_state_sigma=1.0, seed=5)
+    d = inputs.draw(w)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    q = torch.empty((N, T, HK, S), device="cuda")
+    k = torch.empty((N, T, HK, S), device="cuda")
+    g = torch.empty((N, T, H), device="cuda")
+    beta = torch.empty((N, T, H), device="cuda")
+    gdn.gdn_l2norm_gqa(dev(d["q_raw"]), q, w.l2_eps)
+    gdn.gdn_l2norm_gqa(dev(d["k_raw"]), k, w.l2_eps)
+    gdn.gdn_decay_gate(dev(d["a"]), dev(d["dt_bias"]), dev(d["A_log"]), g)
+    gdn.gdn_sigmoid(dev(d["b"]), beta)
+    v, st, x, cw, cs = (dev(d[key]) for key in ("v", "state", "x", "conv_w", "conv_state"))
+    y = torch.empty((N, T, H, S), device="cuda")
+    co = torch.empty_like(x)
+    snaps = torch.empty((N, T, H, S, S), device="cuda")
+    csnaps = torch.empty((N, T, C, K - 1), device="cuda")
+
+    def step():
+        gdn.gdn_conv1d_silu_seq_ex(x, cw, cs, co, csnaps)
+        gdn.gdn_recurrence_seq_ex(st, q, k, v, g, beta, y, w.scale, snaps)
+
+    for _ in range(warmup):
+        step()
+    with Timer(torch) as tm:
+        for _ in range(steps):
+            step()
+    ms = tm.wall_ms / steps
+    nbytes = (2 * N * H * S * S * 4 + N * T * H * S * S * 4      # state r+w, snapshots
+              + 2 * N * T * HK * S * 4 + 2 * N * T * H * S * 4     # q, k; v, y
+              + 2 * N * T * C * 4 + 2 * N * C * (K - 1) * 4 + N * T * C * (K - 1) * 4)
+    return {"workload": "speculative verify: 64 sequences x 4 draft tokens, 16 -> 32 heads, "
+                        "S=128, conv C=8192 K=4, state and history snapshots per token",
+            "ms_per_step": ms, "tokens_per_s": N * T / (ms * 1e-3),
+            "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 def block_layer_bytes(N, H, HK, S, K) -> int:
@@ -385,6 +435,15 @@ def main():
         _, _, full = run_decode(torch, gdn, inputs, K, W, with_glue=True)
         out_legs["decode_full"] = {"ms_per_step": full["ms_per_step"],
                                    "state_GBps": full["state_GBps"]}
+        torch.cuda.empty_cache()
+    if "decode_t4" in legs:
+        log("leg decode_t4")
+        _, _, t4 = run_decode(torch, gdn, inputs, K, W, t4=True)
+        out_legs["decode_t4"] = {"ms_per_step": t4["ms_per_step"], "state_GBps": t4["state_GBps"]}
+        torch.cuda.empty_cache()
+    if "spec" in legs:
+        log("leg spec: 64 seqs x 4 draft tokens with snapshots")
+        out_legs["spec"] = run_spec(torch, gdn, inputs, K, W)
         torch.cuda.empty_cache()
     if "scan" in legs:
         log("leg scan: conv 4096x8192 + recurrence T=4096")

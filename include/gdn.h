@@ -153,6 +153,52 @@ int gdn_recurrence_seq(float *state, const float *q, const float *k, const float
                        const float *g, const float *beta, float *y, int n_seqs, int n_tokens,
                        int n_v_heads, int state_size, float scale, void *stream);
 
+/* Read-out variants of gdn_recurrence_ex. */
+#define GDN_RECUR_EXACT 0 /* y = scale * (updated row . q), as gdn_recurrence */
+#define GDN_RECUR_T4 1    /* y = scale * (decayed row . q + delta * (k . q)) */
+
+/*
+ * gdn_recurrence with the grouped-query repeat done by index and a choice of
+ * read-out. V-head h of sequence n reads K-head h mod n_k_heads of q and k
+ * ([MLX] "GQA: tiled mapping"), so q, k are [n_seqs][n_k_heads][S] (pass
+ * n_k_heads = n_v_heads for already-repeated q, k). GDN_RECUR_T4 regroups the
+ * read-out as [CU]'s "T4" kernel (fc_ssm_recurrence_slots_2pass) does:
+ * r_dec . q and r_dec . k are reduced together from the decayed row and
+ * y = scale * (r_dec . q + delta * (k . q)). The state is identical to the
+ * exact variant bit for bit; y differs from it only by rounding.
+ * Errors as gdn_recurrence, plus GDN_ESIZE when n_v_heads is not a multiple
+ * of n_k_heads and GDN_EUNSUPPORTED for an unknown variant.
+ */
+int gdn_recurrence_ex(float *state, const float *q, const float *k, const float *v,
+                      const float *g, const float *beta, float *y, int n_seqs, int n_k_heads,
+                      int n_v_heads, int state_size, float scale, int variant, void *stream);
+
+/*
+ * gdn_recurrence_seq with the grouped-query repeat done by index (q, k are
+ * [n_seqs][n_tokens][n_k_heads][S]) and optional per-token snapshots for
+ * speculative decoding ([CU] fc_ssm_recurrence_seq, "snaps"): when snaps is
+ * not NULL, snaps[n][t] (n_v_heads*S*S floats, the state layout) receives the
+ * state after token t of sequence n, so a caller that accepts the first M
+ * tokens restores snaps[n][M-1]. snaps [n_seqs][n_tokens][n_v_heads][S][S],
+ * 16-byte aligned, caller-owned. Errors as gdn_recurrence_seq.
+ */
+int gdn_recurrence_seq_ex(float *state, const float *q, const float *k, const float *v,
+                          const float *g, const float *beta, float *y, float *snaps, int n_seqs,
+                          int n_tokens, int n_k_heads, int n_v_heads, int state_size, float scale,
+                          void *stream);
+
+/*
+ * gdn_conv1d_silu_seq with optional per-position history snapshots ([CU]
+ * fc_ssm_conv1d_silu_seq, "snaps"): when snaps is not NULL, snaps[n][t]
+ * (conv_dim*(conv_kernel-1) floats, the conv_state layout) receives the
+ * history after position t of sequence n.
+ *   snaps [n_seqs][n_tokens][conv_dim][conv_kernel - 1], caller-owned.
+ * Errors as gdn_conv1d_silu_seq.
+ */
+int gdn_conv1d_silu_seq_ex(const float *x, const float *w, float *conv_state, float *out,
+                           float *snaps, int n_seqs, int n_tokens, int conv_dim, int conv_kernel,
+                           void *stream);
+
 /*
  * Gated RMSNorm ([FM] "Gated RMSNorm"; [CU] Kernel 3): per row of head_dim
  * values, out = y / sqrt(mean(y^2) + eps) * w * silu(z), silu(z) =

@@ -43,12 +43,16 @@ __global__ __launch_bounds__(256) void conv_step_kernel(const float* __restrict_
 }
 
 // Scan: block (cb, chunk, n) covers channels cb*256 .. +255 and positions
-// chunk*TB .. +TB-1 of sequence n.
-template <int K, int TB>
+// chunk*TB .. +TB-1 of sequence n. With SNAP the history after every position
+// t is also written to snaps[N][T][C][K-1] (the conv_state layout, one image
+// per position), for speculative decoding's partial accept (ssm_gated_delta.cu
+// fc_ssm_conv1d_silu_seq, "snaps").
+template <int K, int TB, bool SNAP>
 __global__ __launch_bounds__(256) void conv_scan_kernel(const float* __restrict__ x,
                                                         const float* __restrict__ w,
                                                         float* __restrict__ conv_state,
-                                                        float* __restrict__ out, int n_tokens,
+                                                        float* __restrict__ out,
+                                                        float* __restrict__ snaps, int n_tokens,
                                                         int conv_dim, int c_blocks,
                                                         int t_chunks) {
   const int cb = blockIdx.x % c_blocks;
@@ -89,6 +93,11 @@ __global__ __launch_bounds__(256) void conv_scan_kernel(const float* __restrict_
 #pragma unroll
     for (int u = 0; u + 1 < K - 1; ++u) hist[u] = hist[u + 1];
     hist[K - 2] = xv;
+    if constexpr (SNAP) {
+      float* sn = snaps + ((n * n_tokens + t) * conv_dim + c) * (K - 1);
+#pragma unroll
+      for (int u = 0; u < K - 1; ++u) sn[u] = hist[u];
+    }
   }
   if (chunk == 0) {
 #pragma unroll
@@ -119,15 +128,19 @@ static int launch_conv_step(const float* x, const float* w, float* cs, float* ou
 }
 
 template <int K>
-static int launch_conv_scan(const float* x, const float* w, float* cs, float* out, int n_seqs,
-                            int n_tokens, int conv_dim, hipStream_t s) {
+static int launch_conv_scan(const float* x, const float* w, float* cs, float* out, float* snaps,
+                            int n_seqs, int n_tokens, int conv_dim, hipStream_t s) {
   constexpr int TB = 16;
   const int c_blocks = (conv_dim + 255) / 256;
   const int t_chunks = (n_tokens + TB - 1) / TB;
   const int64_t blocks = (int64_t)n_seqs * c_blocks * t_chunks;
   if (blocks >= (int64_t(1) << 31)) return GDN_ESIZE;
-  hipLaunchKernelGGL((conv_scan_kernel<K, TB>), dim3((unsigned)blocks), dim3(256), 0, s, x, w, cs,
-                     out, n_tokens, conv_dim, c_blocks, t_chunks);
+  if (snaps)
+    hipLaunchKernelGGL((conv_scan_kernel<K, TB, true>), dim3((unsigned)blocks), dim3(256), 0, s, x,
+                       w, cs, out, snaps, n_tokens, conv_dim, c_blocks, t_chunks);
+  else
+    hipLaunchKernelGGL((conv_scan_kernel<K, TB, false>), dim3((unsigned)blocks), dim3(256), 0, s,
+                       x, w, cs, out, nullptr, n_tokens, conv_dim, c_blocks, t_chunks);
   return launch_status();
 }
 
@@ -148,16 +161,32 @@ extern "C" int gdn_conv1d_silu(const float* x, const float* w, float* conv_state
   return GDN_EUNSUPPORTED;
 }
 
+static int conv_seq(const float* x, const float* w, float* conv_state, float* out, float* snaps,
+                    int n_seqs, int n_tokens, int conv_dim, int conv_kernel, hipStream_t s) {
+  switch (conv_kernel) {
+    case 2: return launch_conv_scan<2>(x, w, conv_state, out, snaps, n_seqs, n_tokens, conv_dim, s);
+    case 3: return launch_conv_scan<3>(x, w, conv_state, out, snaps, n_seqs, n_tokens, conv_dim, s);
+    case 4: return launch_conv_scan<4>(x, w, conv_state, out, snaps, n_seqs, n_tokens, conv_dim, s);
+  }
+  return GDN_EUNSUPPORTED;
+}
+
 extern "C" int gdn_conv1d_silu_seq(const float* x, const float* w, float* conv_state, float* out,
                                    int n_seqs, int n_tokens, int conv_dim, int conv_kernel,
                                    void* stream) {
   const int rc = check_conv(x, w, conv_state, out, n_seqs, n_tokens, conv_dim, conv_kernel);
   if (rc != GDN_OK) return finish_check(rc);
-  hipStream_t s = as_stream(stream);
-  switch (conv_kernel) {
-    case 2: return launch_conv_scan<2>(x, w, conv_state, out, n_seqs, n_tokens, conv_dim, s);
-    case 3: return launch_conv_scan<3>(x, w, conv_state, out, n_seqs, n_tokens, conv_dim, s);
-    case 4: return launch_conv_scan<4>(x, w, conv_state, out, n_seqs, n_tokens, conv_dim, s);
-  }
-  return GDN_EUNSUPPORTED;
+  return conv_seq(x, w, conv_state, out, nullptr, n_seqs, n_tokens, conv_dim, conv_kernel,
+                  as_stream(stream));
+}
+
+extern "C" int gdn_conv1d_silu_seq_ex(const float* x, const float* w, float* conv_state,
+                                      float* out, float* snaps, int n_seqs, int n_tokens,
+                                      int conv_dim, int conv_kernel, void* stream) {
+  const int rc = check_conv(x, w, conv_state, out, n_seqs, n_tokens, conv_dim, conv_kernel);
+  if (rc != GDN_OK) return finish_check(rc);
+  int64_t e;
+  if (snaps && !mul_ok((int64_t)n_seqs * n_tokens * conv_dim, conv_kernel - 1, &e)) return GDN_ESIZE;
+  return conv_seq(x, w, conv_state, out, snaps, n_seqs, n_tokens, conv_dim, conv_kernel,
+                  as_stream(stream));
 }

@@ -143,6 +143,27 @@ __device__ __forceinline__ float delta_rule_step(float (&r)[E], const float (&k)
   return scale * o;
 }
 
+// The same token with the read-out regrouped as in the "T4" kernel of
+// ssm_gated_delta.cu (fc_ssm_recurrence_slots_2pass): after the decay,
+//   y = scale * (r_dec . q + delta * (k . q)),
+// so pred = r_dec . k and r_dec . q are reduced together from the decayed row
+// and no dot product waits on the update. qk = k . q is the same for every row
+// of the head and is passed in. The state trajectory is identical to
+// delta_rule_step's bit for bit; only y is reassociated.
+template <int E, int L>
+__device__ __forceinline__ float delta_rule_step_t4(float (&r)[E], const float (&k)[E],
+                                                    const float (&q)[E], float v, float d, float beta,
+                                                    float qk, float scale) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) r[e] = r[e] * d;
+  const float pred = group_sum<L>(lane_dot<E>(r, k));
+  const float oq = group_sum<L>(lane_dot<E>(r, q));
+  const float delta = (v - pred) * beta;
+#pragma unroll
+  for (int e = 0; e < E; ++e) r[e] = __builtin_fmaf(k[e], delta, r[e]);
+  return scale * __builtin_fmaf(delta, qk, oq);
+}
+
 // One output of the causal conv1d + SiLU: the newest tap first,
 // x * w[K-1], then history[u] * w[u] for ascending u (oldest first), then SiLU.
 template <int K>

@@ -32,11 +32,15 @@ namespace gdn {
 // ---------------------------------------------------------------------------
 constexpr int kDecodeWaves = 8;
 
-template <int S, int RW>
+// With T4 the read-out is regrouped as y = scale * (r_dec . q + delta * qk)
+// (delta_rule_step_t4); qk = k . q is reduced once per wave. The state is the
+// same either way. V-head h of sequence n reads K-head h mod n_k_heads of q
+// and k (the tiled grouped-query repeat), so q and k are [N][HK][S].
+template <int S, int RW, bool T4>
 __global__ __launch_bounds__(64 * kDecodeWaves) void recurrence_decode_kernel(
     float* __restrict__ state, const float* __restrict__ q, const float* __restrict__ k,
     const float* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
-    float* __restrict__ y, int64_t n_pairs, float scale) {
+    float* __restrict__ y, int64_t n_pairs, int n_k_heads, int n_v_heads, float scale) {
   using Lay = RecurLayout<S>;
   constexpr int E = Lay::E, L = Lay::L, G = Lay::G;
   constexpr int IT = RW / G;         // row groups per wave
@@ -45,16 +49,19 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void recurrence_decode_kernel(
 
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int64_t pair = wave / WPH;
+  const int64_t pair = wave / WPH;   // n * H + h
   if (pair >= n_pairs) return;  // uniform across the wave; the kernel has no barrier
   const int p = lane % L;
   const int row0 = (int)(wave % WPH) * RW + lane / L;
+  const int64_t kq = (pair / n_v_heads) * n_k_heads + (pair % n_v_heads) % n_k_heads;
 
   float kk[E], qq[E];
-  load_row_part<E, L>(k + pair * S, p, kk);
-  load_row_part<E, L>(q + pair * S, p, qq);
+  load_row_part<E, L>(k + kq * S, p, kk);
+  load_row_part<E, L>(q + kq * S, p, qq);
   const float d = expf(g[pair]);
   const float b = beta[pair];
+  float qk = 0.0f;
+  if constexpr (T4) qk = group_sum<L>(lane_dot<E>(kk, qq));
 
   float* sp = state + pair * (int64_t)S * S;
   float4 raw[IT][E / 4];
@@ -71,7 +78,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void recurrence_decode_kernel(
   for (int it = 0; it < IT; ++it) {
     float r[E];
     unpack<E>(raw[it], r);
-    const float yj = delta_rule_step<E, L>(r, kk, qq, vv[it], d, b, scale);
+    float yj;
+    if constexpr (T4)
+      yj = delta_rule_step_t4<E, L>(r, kk, qq, vv[it], d, b, qk, scale);
+    else
+      yj = delta_rule_step<E, L>(r, kk, qq, vv[it], d, b, scale);
     float* rp = sp + (int64_t)(row0 + it * G) * S;
 #pragma unroll
     for (int m = 0; m < E / 4; ++m)
@@ -87,15 +98,126 @@ template <> struct DecodeCfg<64> { static constexpr int RW = 8; };
 template <> struct DecodeCfg<128> { static constexpr int RW = 8; };
 template <> struct DecodeCfg<256> { static constexpr int RW = 8; };
 
-template <int S>
+template <int S, bool T4>
 static int launch_decode(float* state, const float* q, const float* k, const float* v,
-                         const float* g, const float* beta, float* y, int64_t n_pairs,
-                         float scale, hipStream_t stream) {
+                         const float* g, const float* beta, float* y, int n_seqs, int n_k_heads,
+                         int n_v_heads, float scale, hipStream_t stream) {
   constexpr int RW = DecodeCfg<S>::RW;
+  const int64_t n_pairs = (int64_t)n_seqs * n_v_heads;
   const int64_t waves = n_pairs * (S / RW);
   const unsigned blocks = grid_for(waves, kDecodeWaves);
-  hipLaunchKernelGGL((recurrence_decode_kernel<S, RW>), dim3(blocks), dim3(64 * kDecodeWaves),
-                     0, stream, state, q, k, v, g, beta, y, n_pairs, scale);
+  hipLaunchKernelGGL((recurrence_decode_kernel<S, RW, T4>), dim3(blocks), dim3(64 * kDecodeWaves),
+                     0, stream, state, q, k, v, g, beta, y, n_pairs, n_k_heads, n_v_heads, scale);
+  return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// Short scan (n_tokens <= kShortScan): the decode kernel's layout with a token
+// loop. Each wave keeps its RW rows in VGPRs for all tokens and reads k, q, v,
+// g and beta of each token straight from memory (they stay in L2: every wave
+// of the head reads the same 1 KiB of k and q), prefetching token t+1 while it
+// computes token t. No LDS and no barrier, so a launch with many sequences and
+// few tokens (a speculative-decoding verify step) streams like the decode; the
+// LDS-staged scan below is for long sequences. Same step function, so the
+// result equals chained decode launches bit for bit.
+// ---------------------------------------------------------------------------
+constexpr int kShortScan = 16;
+
+template <int S, int RW, bool SNAP>
+__global__ __launch_bounds__(64 * kDecodeWaves) void recurrence_short_scan_kernel(
+    float* __restrict__ state, const float* __restrict__ q, const float* __restrict__ k,
+    const float* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
+    float* __restrict__ y, float* __restrict__ snaps, int64_t n_pairs, int n_tokens,
+    int n_k_heads, int n_v_heads, float scale) {
+  using Lay = RecurLayout<S>;
+  constexpr int E = Lay::E, L = Lay::L, G = Lay::G;
+  constexpr int IT = RW / G;
+  constexpr int WPH = S / RW;
+  static_assert(RW % G == 0 && S % RW == 0, "rows per wave must tile the head");
+
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t pair = wave / WPH;   // n * H + h
+  if (pair >= n_pairs) return;  // uniform across the wave; the kernel has no barrier
+  const int p = lane % L;
+  const int row0 = (int)(wave % WPH) * RW + lane / L;
+  const int64_t n = pair / n_v_heads;
+  const int h = (int)(pair % n_v_heads);
+  const int kh = h % n_k_heads;
+  const int64_t tok_v = (int64_t)n_v_heads * S, tok_k = (int64_t)n_k_heads * S;
+  const float* qn = q + n * n_tokens * tok_k + (int64_t)kh * S;
+  const float* kn = k + n * n_tokens * tok_k + (int64_t)kh * S;
+  const float* vn = v + n * n_tokens * tok_v + (int64_t)h * S + row0;
+  float* yn = y + n * n_tokens * tok_v + (int64_t)h * S + row0;
+  const float* gn = g + n * n_tokens * n_v_heads + h;
+  const float* bn = beta + n * n_tokens * n_v_heads + h;
+
+  float* sp = state + pair * (int64_t)S * S;
+  float r[IT][E];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    float4 raw[E / 4];
+#pragma unroll
+    for (int m = 0; m < E / 4; ++m)
+      raw[m] = load4_stream(sp + (int64_t)(row0 + it * G) * S + 4 * (p + L * m));
+    unpack<E>(raw, r[it]);
+  }
+
+  float kk[E], qq[E], vv[IT], gg, bb;
+  auto read = [&](int t) {
+    load_row_part<E, L>(kn + t * tok_k, p, kk);
+    load_row_part<E, L>(qn + t * tok_k, p, qq);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) vv[it] = vn[t * tok_v + it * G];
+    gg = gn[(int64_t)t * n_v_heads];
+    bb = bn[(int64_t)t * n_v_heads];
+  };
+  read(0);
+  for (int t = 0; t < n_tokens; ++t) {
+    float kc[E], qc[E], vc[IT];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      kc[e] = kk[e];
+      qc[e] = qq[e];
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) vc[it] = vv[it];
+    const float d = expf(gg);
+    const float b = bb;
+    if (t + 1 < n_tokens) read(t + 1);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const float yj = delta_rule_step<E, L>(r[it], kc, qc, vc[it], d, b, scale);
+      if (p == 0) yn[t * tok_v + it * G] = yj;
+      if constexpr (SNAP) {
+        float* sn = snaps + ((n * n_tokens + t) * n_v_heads + h) * (int64_t)S * S +
+                    (int64_t)(row0 + it * G) * S;
+#pragma unroll
+        for (int m = 0; m < E / 4; ++m)
+          store4_stream(sn + 4 * (p + L * m), make_float4(r[it][4 * m], r[it][4 * m + 1],
+                                                          r[it][4 * m + 2], r[it][4 * m + 3]));
+      }
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it)
+#pragma unroll
+    for (int m = 0; m < E / 4; ++m)
+      store4_stream(sp + (int64_t)(row0 + it * G) * S + 4 * (p + L * m),
+                    make_float4(r[it][4 * m], r[it][4 * m + 1], r[it][4 * m + 2], r[it][4 * m + 3]));
+}
+
+template <int S, bool SNAP>
+static int launch_short_scan(float* state, const float* q, const float* k, const float* v,
+                             const float* g, const float* beta, float* y, float* snaps, int n_seqs,
+                             int n_tokens, int n_k_heads, int n_v_heads, float scale,
+                             hipStream_t stream) {
+  constexpr int RW = DecodeCfg<S>::RW;
+  const int64_t n_pairs = (int64_t)n_seqs * n_v_heads;
+  const unsigned blocks = grid_for(n_pairs * (S / RW), kDecodeWaves);
+  hipLaunchKernelGGL((recurrence_short_scan_kernel<S, RW, SNAP>), dim3(blocks),
+                     dim3(64 * kDecodeWaves), 0, stream, state, q, k, v, g, beta, y, snaps, n_pairs,
+                     n_tokens, n_k_heads, n_v_heads, scale);
   return launch_status();
 }
 
@@ -115,6 +237,12 @@ static int launch_decode(float* state, const float* q, const float* k, const flo
 // Block order: the BPH blocks of one head read the same k and q, so they are
 // numbered to land on the same XCD (the hardware deals consecutive block ids
 // round-robin over the 8 XCDs) and share that XCD's L2.
+//
+// V-head h reads K-head h mod n_k_heads of q and k (q, k are [N][T][HK][S]).
+// With SNAP, the state after every token is also written to
+// snaps[N][T][H][S][S] (the state layout, one image per token): a caller that
+// accepts only the first M of T speculative tokens restores image M-1
+// (ssm_gated_delta.cu fc_ssm_recurrence_seq, "snaps").
 // ---------------------------------------------------------------------------
 template <int S>
 struct ScanCfg {
@@ -145,12 +273,13 @@ __device__ __forceinline__ unsigned xcd_group(unsigned bid, unsigned nblocks) {
   return (bid % kXcds) * (nblocks / kXcds) + bid / kXcds;
 }
 
-template <int S>
+template <int S, bool SNAP>
 __global__ __launch_bounds__(ScanCfg<S>::THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void recurrence_scan_kernel(
     float* __restrict__ state, const float* __restrict__ q, const float* __restrict__ k,
     const float* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
-    float* __restrict__ y, int n_tokens, int n_v_heads, float scale) {
+    float* __restrict__ y, float* __restrict__ snaps, int n_tokens, int n_k_heads,
+    int n_v_heads, float scale) {
   using Lay = RecurLayout<S>;
   using Cfg = ScanCfg<S>;
   constexpr int E = Lay::E, L = Lay::L, G = Lay::G;
@@ -170,10 +299,12 @@ void recurrence_scan_kernel(
   const int lrow = wv * G + lane / L;                   // row within the block
   const int row = rblk + lrow;
 
-  const int64_t tok_stride = (int64_t)n_v_heads * S;     // q/k/v/y stride per token
+  const int64_t tok_stride = (int64_t)n_v_heads * S;     // v/y stride per token
+  const int64_t kq_stride = (int64_t)n_k_heads * S;      // q/k stride per token
   const int64_t base_n = n * (int64_t)n_tokens;          // token index of (n, 0)
-  const float* qn = q + base_n * tok_stride + (int64_t)h * S;
-  const float* kn = k + base_n * tok_stride + (int64_t)h * S;
+  const int kh = h % n_k_heads;
+  const float* qn = q + base_n * kq_stride + (int64_t)kh * S;
+  const float* kn = k + base_n * kq_stride + (int64_t)kh * S;
   const float* vn = v + base_n * tok_stride + (int64_t)h * S + rblk;
   float* yn = y + base_n * tok_stride + (int64_t)h * S + rblk;
   const float* gn = g + base_n * n_v_heads + h;
@@ -191,8 +322,8 @@ void recurrence_scan_kernel(
       const int f = (i * THREADS + tid) * 4;   // float index inside [CT][S]
       const int tt = f / S, col = f % S;
       if (tt < ct) {
-        pk[i] = load4(kn + (int64_t)(t0 + tt) * tok_stride + col);
-        pq[i] = load4(qn + (int64_t)(t0 + tt) * tok_stride + col);
+        pk[i] = load4(kn + (int64_t)(t0 + tt) * kq_stride + col);
+        pq[i] = load4(qn + (int64_t)(t0 + tt) * kq_stride + col);
       }
     }
 #pragma unroll
@@ -230,6 +361,18 @@ void recurrence_scan_kernel(
   float r[E];
   float* srow = state + head * (int64_t)S * S + (int64_t)row * S;
   load_row_part<E, L>(srow, p, r);
+  // snapshot of token t: snaps[((n*T + t)*H + h)*S*S + row*S + ...]
+  float* snap_row = SNAP ? snaps + (base_n * n_v_heads + h) * (int64_t)S * S + (int64_t)row * S
+                         : nullptr;
+  const int64_t snap_stride = (int64_t)n_v_heads * S * S;
+  auto snapshot = [&](int t) {
+    if constexpr (SNAP) {
+#pragma unroll
+      for (int m = 0; m < E / 4; ++m)
+        store4_stream(snap_row + t * snap_stride + 4 * (p + L * m),
+                      make_float4(r[4 * m], r[4 * m + 1], r[4 * m + 2], r[4 * m + 3]));
+    }
+  };
 
   // One token of the chunk in buffer `buf`; y goes to ysm (every lane of the
   // row writes the same value).
@@ -244,7 +387,7 @@ void recurrence_scan_kernel(
   };
   // A full chunk with the next token's LDS reads issued before the current
   // token's arithmetic (two register sets, rotated by the unrolled loop).
-  auto full_chunk = [&](const float* buf) {
+  auto full_chunk = [&](const float* buf, int t0) {
     float kk[2][E], qq[2][E], vj[2], d[2], b[2];
     auto read = [&](int tt, int slot) {
       load_row_part<E, L>(buf + tt * S, p, kk[slot]);
@@ -259,6 +402,7 @@ void recurrence_scan_kernel(
       const int cur = tt & 1;
       if (tt + 1 < CT) read(tt + 1, cur ^ 1);
       ysm[tt * R + lrow] = delta_rule_step<E, L>(r, kk[cur], qq[cur], vj[cur], d[cur], b[cur], scale);
+      snapshot(t0 + tt);
     }
   };
 
@@ -273,9 +417,12 @@ void recurrence_scan_kernel(
     if (more) fetch(t0 + CT);
     const float* buf = smem + buf_id * BUF;
     if (ct == CT) {
-      full_chunk(buf);
+      full_chunk(buf, t0);
     } else {
-      for (int tt = 0; tt < ct; ++tt) token(buf, tt);
+      for (int tt = 0; tt < ct; ++tt) {
+        token(buf, tt);
+        snapshot(t0 + tt);
+      }
     }
     if (more) deposit(smem + (buf_id ^ 1) * BUF, t0 + CT);
     __syncthreads();
@@ -293,21 +440,27 @@ void recurrence_scan_kernel(
     store4(srow + 4 * (p + L * m), make_float4(r[4 * m], r[4 * m + 1], r[4 * m + 2], r[4 * m + 3]));
 }
 
-template <int S>
+template <int S, bool SNAP>
 static int launch_scan(float* state, const float* q, const float* k, const float* v,
-                       const float* g, const float* beta, float* y, int n_seqs, int n_tokens,
-                       int n_v_heads, float scale, hipStream_t stream) {
+                       const float* g, const float* beta, float* y, float* snaps, int n_seqs,
+                       int n_tokens, int n_k_heads, int n_v_heads, float scale, hipStream_t stream) {
+  if (n_tokens <= kShortScan)
+    return launch_short_scan<S, SNAP>(state, q, k, v, g, beta, y, snaps, n_seqs, n_tokens,
+                                      n_k_heads, n_v_heads, scale, stream);
   using Cfg = ScanCfg<S>;
   const int64_t blocks = (int64_t)n_seqs * n_v_heads * Cfg::BPH;
-  hipLaunchKernelGGL((recurrence_scan_kernel<S>), dim3((unsigned)blocks), dim3(Cfg::THREADS), 0,
-                     stream, state, q, k, v, g, beta, y, n_tokens, n_v_heads, scale);
+  hipLaunchKernelGGL((recurrence_scan_kernel<S, SNAP>), dim3((unsigned)blocks), dim3(Cfg::THREADS),
+                     0, stream, state, q, k, v, g, beta, y, snaps, n_tokens, n_k_heads, n_v_heads,
+                     scale);
   return launch_status();
 }
 
 static int check_recurrence(float* state, const float* q, const float* k, const float* v,
                             const float* g, const float* beta, float* y, int n_seqs,
-                            int n_tokens, int n_v_heads, int state_size) {
-  if (n_seqs < 0 || n_tokens < 0 || n_v_heads <= 0 || state_size <= 0) return GDN_ESIZE;
+                            int n_tokens, int n_k_heads, int n_v_heads, int state_size) {
+  if (n_seqs < 0 || n_tokens < 0 || n_k_heads <= 0 || n_v_heads <= 0 || state_size <= 0)
+    return GDN_ESIZE;
+  if (n_v_heads % n_k_heads != 0) return GDN_ESIZE;
   if (!is_state_size(state_size)) return GDN_EUNSUPPORTED;
   if (n_seqs == 0 || n_tokens == 0) return kNothingToDo;
   if (!state || !q || !k || !v || !g || !beta || !y) return GDN_ENULL;
@@ -320,6 +473,34 @@ static int check_recurrence(float* state, const float* q, const float* k, const 
   return GDN_OK;
 }
 
+template <bool T4>
+static int dispatch_decode(float* state, const float* q, const float* k, const float* v,
+                           const float* g, const float* beta, float* y, int n_seqs,
+                           int n_k_heads, int n_v_heads, int state_size, float scale,
+                           hipStream_t s) {
+  switch (state_size) {
+    case 32: return launch_decode<32, T4>(state, q, k, v, g, beta, y, n_seqs, n_k_heads, n_v_heads, scale, s);
+    case 64: return launch_decode<64, T4>(state, q, k, v, g, beta, y, n_seqs, n_k_heads, n_v_heads, scale, s);
+    case 128: return launch_decode<128, T4>(state, q, k, v, g, beta, y, n_seqs, n_k_heads, n_v_heads, scale, s);
+    case 256: return launch_decode<256, T4>(state, q, k, v, g, beta, y, n_seqs, n_k_heads, n_v_heads, scale, s);
+  }
+  return GDN_EUNSUPPORTED;
+}
+
+template <bool SNAP>
+static int dispatch_scan(float* state, const float* q, const float* k, const float* v,
+                         const float* g, const float* beta, float* y, float* snaps, int n_seqs,
+                         int n_tokens, int n_k_heads, int n_v_heads, int state_size, float scale,
+                         hipStream_t s) {
+  switch (state_size) {
+    case 32: return launch_scan<32, SNAP>(state, q, k, v, g, beta, y, snaps, n_seqs, n_tokens, n_k_heads, n_v_heads, scale, s);
+    case 64: return launch_scan<64, SNAP>(state, q, k, v, g, beta, y, snaps, n_seqs, n_tokens, n_k_heads, n_v_heads, scale, s);
+    case 128: return launch_scan<128, SNAP>(state, q, k, v, g, beta, y, snaps, n_seqs, n_tokens, n_k_heads, n_v_heads, scale, s);
+    case 256: return launch_scan<256, SNAP>(state, q, k, v, g, beta, y, snaps, n_seqs, n_tokens, n_k_heads, n_v_heads, scale, s);
+  }
+  return GDN_EUNSUPPORTED;
+}
+
 }  // namespace gdn
 
 using namespace gdn;
@@ -327,32 +508,56 @@ using namespace gdn;
 extern "C" int gdn_recurrence(float* state, const float* q, const float* k, const float* v,
                               const float* g, const float* beta, float* y, int n_seqs,
                               int n_v_heads, int state_size, float scale, void* stream) {
-  const int rc = check_recurrence(state, q, k, v, g, beta, y, n_seqs, 1, n_v_heads, state_size);
+  const int rc = check_recurrence(state, q, k, v, g, beta, y, n_seqs, 1, n_v_heads, n_v_heads,
+                                  state_size);
   if (rc != GDN_OK) return finish_check(rc);
-  const int64_t pairs = (int64_t)n_seqs * n_v_heads;
+  return dispatch_decode<false>(state, q, k, v, g, beta, y, n_seqs, n_v_heads, n_v_heads,
+                                state_size, scale, as_stream(stream));
+}
+
+extern "C" int gdn_recurrence_ex(float* state, const float* q, const float* k, const float* v,
+                                 const float* g, const float* beta, float* y, int n_seqs,
+                                 int n_k_heads, int n_v_heads, int state_size, float scale,
+                                 int variant, void* stream) {
+  if (variant != GDN_RECUR_EXACT && variant != GDN_RECUR_T4) return GDN_EUNSUPPORTED;
+  const int rc = check_recurrence(state, q, k, v, g, beta, y, n_seqs, 1, n_k_heads, n_v_heads,
+                                  state_size);
+  if (rc != GDN_OK) return finish_check(rc);
   hipStream_t s = as_stream(stream);
-  switch (state_size) {
-    case 32: return launch_decode<32>(state, q, k, v, g, beta, y, pairs, scale, s);
-    case 64: return launch_decode<64>(state, q, k, v, g, beta, y, pairs, scale, s);
-    case 128: return launch_decode<128>(state, q, k, v, g, beta, y, pairs, scale, s);
-    case 256: return launch_decode<256>(state, q, k, v, g, beta, y, pairs, scale, s);
-  }
-  return GDN_EUNSUPPORTED;
+  if (variant == GDN_RECUR_T4)
+    return dispatch_decode<true>(state, q, k, v, g, beta, y, n_seqs, n_k_heads, n_v_heads,
+                                 state_size, scale, s);
+  return dispatch_decode<false>(state, q, k, v, g, beta, y, n_seqs, n_k_heads, n_v_heads,
+                                state_size, scale, s);
 }
 
 extern "C" int gdn_recurrence_seq(float* state, const float* q, const float* k, const float* v,
                                   const float* g, const float* beta, float* y, int n_seqs,
                                   int n_tokens, int n_v_heads, int state_size, float scale,
                                   void* stream) {
-  const int rc =
-      check_recurrence(state, q, k, v, g, beta, y, n_seqs, n_tokens, n_v_heads, state_size);
+  const int rc = check_recurrence(state, q, k, v, g, beta, y, n_seqs, n_tokens, n_v_heads,
+                                  n_v_heads, state_size);
   if (rc != GDN_OK) return finish_check(rc);
+  return dispatch_scan<false>(state, q, k, v, g, beta, y, nullptr, n_seqs, n_tokens, n_v_heads,
+                              n_v_heads, state_size, scale, as_stream(stream));
+}
+
+extern "C" int gdn_recurrence_seq_ex(float* state, const float* q, const float* k,
+                                     const float* v, const float* g, const float* beta, float* y,
+                                     float* snaps, int n_seqs, int n_tokens, int n_k_heads,
+                                     int n_v_heads, int state_size, float scale, void* stream) {
+  const int rc = check_recurrence(state, q, k, v, g, beta, y, n_seqs, n_tokens, n_k_heads,
+                                  n_v_heads, state_size);
+  if (rc != GDN_OK) return finish_check(rc);
+  if (snaps && !aligned16(snaps)) return GDN_EALIGN;
+  int64_t snap_elems;
+  if (snaps && !mul_ok((int64_t)n_seqs * n_tokens * n_v_heads, (int64_t)state_size * state_size,
+                       &snap_elems))
+    return GDN_ESIZE;
   hipStream_t s = as_stream(stream);
-  switch (state_size) {
-    case 32: return launch_scan<32>(state, q, k, v, g, beta, y, n_seqs, n_tokens, n_v_heads, scale, s);
-    case 64: return launch_scan<64>(state, q, k, v, g, beta, y, n_seqs, n_tokens, n_v_heads, scale, s);
-    case 128: return launch_scan<128>(state, q, k, v, g, beta, y, n_seqs, n_tokens, n_v_heads, scale, s);
-    case 256: return launch_scan<256>(state, q, k, v, g, beta, y, n_seqs, n_tokens, n_v_heads, scale, s);
-  }
-  return GDN_EUNSUPPORTED;
+  if (snaps)
+    return dispatch_scan<true>(state, q, k, v, g, beta, y, snaps, n_seqs, n_tokens, n_k_heads,
+                               n_v_heads, state_size, scale, s);
+  return dispatch_scan<false>(state, q, k, v, g, beta, y, nullptr, n_seqs, n_tokens, n_k_heads,
+                              n_v_heads, state_size, scale, s);
 }

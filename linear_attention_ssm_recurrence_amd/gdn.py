@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "gdn.h")
 
 GDN_OK, GDN_ENULL, GDN_ESIZE, GDN_EUNSUPPORTED, GDN_EALIGN, GDN_ELAUNCH = range(6)
+GDN_RECUR_EXACT, GDN_RECUR_T4 = 0, 1
 
 
 class GdnError(RuntimeError):
@@ -52,6 +53,9 @@ def load_library():
         "gdn_conv1d_silu": [P, P, P, P, I, I, I, P],
         "gdn_conv1d_silu_seq": [P, P, P, P, I, I, I, I, P],
         "gdn_recurrence": [P, P, P, P, P, P, P, I, I, I, F, P],
+        "gdn_recurrence_ex": [P, P, P, P, P, P, P, I, I, I, I, F, I, P],
+        "gdn_recurrence_seq_ex": [P, P, P, P, P, P, P, P, I, I, I, I, I, F, P],
+        "gdn_conv1d_silu_seq_ex": [P, P, P, P, P, I, I, I, I, P],
         "gdn_recurrence_seq": [P, P, P, P, P, P, P, I, I, I, I, F, P],
         "gdn_gated_rmsnorm": [P, P, P, P, L, I, F, P],
         "gdn_decode_block_bf16": [P] * 11 + [I] * 5 + [F] * 3 + [P],
@@ -181,6 +185,59 @@ def gdn_recurrence_seq(state, q, k, v, g, beta, y, scale, stream=None):
     _call("gdn_recurrence_seq", _ptr(state, F32, "state"), _ptr(q, F32, "q"), _ptr(k, F32, "k"),
           _ptr(v, F32, "v"), _ptr(g, F32, "g"), _ptr(beta, F32, "beta"), _ptr(y, F32, "y"),
           N, T, H, S, float(scale), _stream(q, stream))
+
+
+def gdn_recurrence_ex(state, q, k, v, g, beta, y, scale, variant=GDN_RECUR_EXACT, stream=None):
+    """state [N][H][S][S] in place; q, k [N][HK][S] (V-head h reads K-head
+    h mod HK); v, y [N][H][S]; g, beta [N][H]."""
+    N, H, S = v.shape
+    HK = q.shape[1]
+    _shape(state, (N, H, S, S), "state")
+    _shape(q, (N, HK, S), "q")
+    _shape(k, (N, HK, S), "k")
+    _shape(y, (N, H, S), "y")
+    _shape(g, (N, H), "g")
+    _shape(beta, (N, H), "beta")
+    _call("gdn_recurrence_ex", _ptr(state, F32, "state"), _ptr(q, F32, "q"), _ptr(k, F32, "k"),
+          _ptr(v, F32, "v"), _ptr(g, F32, "g"), _ptr(beta, F32, "beta"), _ptr(y, F32, "y"),
+          N, HK, H, S, float(scale), int(variant), _stream(v, stream))
+
+
+def gdn_recurrence_seq_ex(state, q, k, v, g, beta, y, scale, snaps=None, stream=None):
+    """state [N][H][S][S] in place; q, k [N][T][HK][S]; v, y [N][T][H][S];
+    g, beta [N][T][H]; snaps None or [N][T][H][S][S] (state after each token)."""
+    N, T, H, S = v.shape
+    HK = q.shape[2]
+    _shape(state, (N, H, S, S), "state")
+    _shape(q, (N, T, HK, S), "q")
+    _shape(k, (N, T, HK, S), "k")
+    _shape(y, (N, T, H, S), "y")
+    _shape(g, (N, T, H), "g")
+    _shape(beta, (N, T, H), "beta")
+    sp = None
+    if snaps is not None:
+        _shape(snaps, (N, T, H, S, S), "snaps")
+        sp = _ptr(snaps, F32, "snaps")
+    _call("gdn_recurrence_seq_ex", _ptr(state, F32, "state"), _ptr(q, F32, "q"), _ptr(k, F32, "k"),
+          _ptr(v, F32, "v"), _ptr(g, F32, "g"), _ptr(beta, F32, "beta"), _ptr(y, F32, "y"), sp,
+          N, T, HK, H, S, float(scale), _stream(v, stream))
+
+
+def gdn_conv1d_silu_seq_ex(x, w, conv_state, out, snaps=None, stream=None):
+    """gdn_conv1d_silu_seq with snaps None or [N][T][C][K-1] (history after
+    each position)."""
+    N, T, C = x.shape
+    K = w.shape[1]
+    _shape(w, (C, K), "w")
+    _shape(conv_state, (N, C, K - 1), "conv_state")
+    _shape(out, (N, T, C), "out")
+    sp = None
+    if snaps is not None:
+        _shape(snaps, (N, T, C, K - 1), "snaps")
+        sp = _ptr(snaps, F32, "snaps")
+    _call("gdn_conv1d_silu_seq_ex", _ptr(x, F32, "x"), _ptr(w, F32, "w"),
+          _ptr(conv_state, F32, "conv_state"), _ptr(out, F32, "out"), sp, N, T, C, K,
+          _stream(x, stream))
 
 
 def gdn_gated_rmsnorm(y, w, z, out, eps=1e-6, stream=None):

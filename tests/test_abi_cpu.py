@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_header_symbol(lib):
     names = gdn.header_symbols()
-    assert len(names) == 11, names
+    assert len(names) == 14, names
     out = os.popen(f"nm -D --defined-only {gdn.LIB_PATH}").read()
     exported = set(re.findall(r"\sT\s(gdn_\w+)", out))
     for name in names:
@@ -113,6 +113,32 @@ def test_pointwise_validation(lib):
     assert nm(FAKE, FAKE, FAKE, FAKE, 1, 34, 1e-6, NUL) == gdn.GDN_EUNSUPPORTED
     assert nm(FAKE, FAKE, FAKE_MIS, FAKE, 1, 32, 1e-6, NUL) == gdn.GDN_EALIGN
     assert nm(NUL, NUL, NUL, NUL, 0, 32, 1e-6, NUL) == gdn.GDN_OK
+
+
+def test_ex_validation(lib):
+    f = lib.gdn_recurrence_ex
+
+    def rex(HK=2, H=4, S=32, variant=0, state=FAKE, n=1):
+        return f(state, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n, HK, H, S, 1.0, variant, NUL)
+
+    assert rex(variant=2) == gdn.GDN_EUNSUPPORTED
+    assert rex(variant=-1) == gdn.GDN_EUNSUPPORTED
+    assert rex(HK=3) == gdn.GDN_ESIZE
+    assert rex(HK=0) == gdn.GDN_ESIZE
+    assert rex(state=NUL) == gdn.GDN_ENULL
+    assert rex(state=NUL, n=0) == gdn.GDN_OK
+    fs = lib.gdn_recurrence_seq_ex
+
+    def rsx(snaps=NUL, HK=2, T=3, n=1):
+        return fs(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, snaps, n, T, HK, 4, 32, 1.0, NUL)
+
+    assert rsx(snaps=FAKE_MIS) == gdn.GDN_EALIGN
+    assert rsx(HK=3) == gdn.GDN_ESIZE
+    assert rsx(T=-1) == gdn.GDN_ESIZE
+    assert rsx(T=0) == gdn.GDN_OK
+    fc = lib.gdn_conv1d_silu_seq_ex
+    assert fc(FAKE, FAKE, FAKE, FAKE, NUL, 1, 1, 8, 5, NUL) == gdn.GDN_EUNSUPPORTED
+    assert fc(NUL, FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 4, NUL) == gdn.GDN_ENULL
 
 
 def test_block_validation(lib):

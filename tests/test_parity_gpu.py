@@ -4,8 +4,9 @@ seeded inputs (needs an MI355X).
 Covers each entry point at the five workloads' shapes (the full sizes of the
 batched decode and the 4096-token scan, and sampled layers of the 64-sequence
 bf16 block in the launch configuration the benchmark times), edge shapes
-(every supported state size, ragged token counts against the scan's 32-token
-chunks, several sequences, conv kernels 2..4 with fewer tokens than taps,
+(every supported state size, token counts on both sides of the 16-token
+switch between the short and the LDS-staged scan and ragged against its
+64-token chunks, several sequences, conv kernels 2..4 with fewer tokens than taps,
 zero vectors, extreme gate inputs, empty inputs), and the bit-level
 properties the pages state: a scan equals chained single steps, and the fused
 layer equals its stages chained.
@@ -82,7 +83,7 @@ def test_tiny_scan_config0():
 
 
 @pytest.mark.parametrize("S", [32, 64, 128, 256])
-@pytest.mark.parametrize("N,T,H", [(1, 1, 1), (2, 33, 3), (1, 70, 2)])
+@pytest.mark.parametrize("N,T,H", [(1, 1, 1), (2, 16, 3), (2, 17, 3), (2, 33, 3), (1, 70, 2)])
 def test_scan_shapes(S, N, T, H):
     rng = np.random.default_rng(1000 + S + 7 * T + N)
     p = _rand_rec(rng, N, T, H, S)

@@ -1,0 +1,123 @@
+"""Parity of the extended entry points (needs an MI355X): the "T4" read-out of
+the decode, the grouped-query repeat done by index in decode and scan, and the
+per-token snapshots of the scan and the conv for speculative decoding.
+
+Each is checked against the oracle within the tolerance, and against the
+plain entry points bit for bit where the arithmetic is the same.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import DEV, assert_close, dev, host, oracle_threads
+from linear_attention_ssm_recurrence_amd import gdn
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdn.load_library()
+    oracle_threads()
+
+
+def _inputs(rng, N, T, HK, H, S):
+    """Recurrence inputs with K-head q/k (unit norm) and their tiled repeat."""
+    qk = oracle.l2norm_gqa(rng.standard_normal((N, T, HK, S)), HK)
+    kk = oracle.l2norm_gqa(rng.standard_normal((N, T, HK, S)), HK)
+    rep = lambda x: np.ascontiguousarray(x[:, :, np.arange(H) % HK, :])
+    v = rng.standard_normal((N, T, H, S)).astype(np.float32)
+    g = oracle.decay_gate(rng.standard_normal((N, T, H)), np.zeros(H), rng.standard_normal(H))
+    beta = oracle.sigmoid(rng.standard_normal((N, T, H)))
+    st = (rng.standard_normal((N, H, S, S)) * 0.05).astype(np.float32)
+    return dict(qh=qk, kh=kk, q=rep(qk), k=rep(kk), v=v, g=g, beta=beta, state=st)
+
+
+@pytest.mark.parametrize("S", [32, 128, 256])
+def test_decode_t4_and_gqa(S):
+    rng = np.random.default_rng(500 + S)
+    N, HK, H = 9, 4, 8
+    p = _inputs(rng, N, 1, HK, H, S)
+    scale = 1 / math.sqrt(S)
+    sq = lambda x: np.ascontiguousarray(x[:, 0])
+    y_ref, st_ref = oracle.recurrence(p["state"], sq(p["q"]), sq(p["k"]), sq(p["v"]), sq(p["g"]),
+                                      sq(p["beta"]), scale)
+    # exact read-out, repeat done by index == plain entry point on repeated q/k
+    st_a, st_b, st_c = dev(p["state"]), dev(p["state"]), dev(p["state"])
+    y_a = torch.empty((N, H, S), device=DEV)
+    y_b = torch.empty_like(y_a)
+    y_c = torch.empty_like(y_a)
+    gdn.gdn_recurrence(st_a, dev(sq(p["q"])), dev(sq(p["k"])), dev(sq(p["v"])), dev(sq(p["g"])),
+                       dev(sq(p["beta"])), y_a, scale)
+    gdn.gdn_recurrence_ex(st_b, dev(sq(p["qh"])), dev(sq(p["kh"])), dev(sq(p["v"])),
+                          dev(sq(p["g"])), dev(sq(p["beta"])), y_b, scale, gdn.GDN_RECUR_EXACT)
+    gdn.gdn_recurrence_ex(st_c, dev(sq(p["qh"])), dev(sq(p["kh"])), dev(sq(p["v"])),
+                          dev(sq(p["g"])), dev(sq(p["beta"])), y_c, scale, gdn.GDN_RECUR_T4)
+    assert torch.equal(st_a, st_b) and torch.equal(y_a, y_b), "index GQA != repeated q/k"
+    # T4: identical state trajectory, y within the tolerance of the oracle
+    assert torch.equal(st_a, st_c), "T4 changed the state"
+    assert_close(host(y_c), y_ref, f"T4 y S={S}")
+    assert_close(host(st_c), st_ref, f"T4 state S={S}")
+
+
+@pytest.mark.parametrize("S,T", [(128, 70), (64, 5), (32, 130)])
+def test_scan_gqa_and_snapshots(S, T):
+    rng = np.random.default_rng(600 + S + T)
+    N, HK, H = 2, 2, 4
+    p = _inputs(rng, N, T, HK, H, S)
+    scale = 1 / math.sqrt(S)
+    # plain scan on repeated q/k
+    st_a = dev(p["state"])
+    y_a = torch.empty((N, T, H, S), device=DEV)
+    gdn.gdn_recurrence_seq(st_a, dev(p["q"]), dev(p["k"]), dev(p["v"]), dev(p["g"]), dev(p["beta"]),
+                           y_a, scale)
+    # extended scan: K-head q/k, snapshots
+    st_b = dev(p["state"])
+    y_b = torch.empty_like(y_a)
+    snaps = torch.full((N, T, H, S, S), float("nan"), device=DEV)
+    gdn.gdn_recurrence_seq_ex(st_b, dev(p["qh"]), dev(p["kh"]), dev(p["v"]), dev(p["g"]),
+                              dev(p["beta"]), y_b, scale, snaps)
+    assert torch.equal(y_a, y_b) and torch.equal(st_a, st_b), "index GQA != repeated q/k"
+    assert torch.equal(snaps[:, T - 1], st_b), "last snapshot != final state"
+    # every snapshot equals the state after that prefix (bits), for a sample of t
+    for t in sorted({0, 1, T // 2, min(63, T - 1), min(64, T - 1), T - 1}):
+        st_t = dev(p["state"])
+        y_t = torch.empty((N, t + 1, H, S), device=DEV)
+        gdn.gdn_recurrence_seq(st_t, dev(p["q"][:, :t + 1]), dev(p["k"][:, :t + 1]),
+                               dev(p["v"][:, :t + 1]), dev(p["g"][:, :t + 1]),
+                               dev(p["beta"][:, :t + 1]), y_t, scale)
+        assert torch.equal(snaps[:, t], st_t), f"snapshot {t} != state after {t + 1} tokens"
+    # and against the oracle, all tokens
+    s = p["state"]
+    sn = host(snaps)
+    for t in range(T):
+        _, s = oracle.recurrence(s, p["q"][:, t], p["k"][:, t], p["v"][:, t], p["g"][:, t],
+                                 p["beta"][:, t], scale)
+        if t % max(1, T // 8) == 0 or t == T - 1:
+            assert_close(sn[:, t], s, f"snapshot {t} vs oracle")
+
+
+@pytest.mark.parametrize("K,T", [(4, 37), (3, 2), (2, 17)])
+def test_conv_snapshots(K, T):
+    rng = np.random.default_rng(700 + K + T)
+    N, C = 2, 300
+    x = rng.standard_normal((N, T, C)).astype(np.float32)
+    w = (rng.standard_normal((C, K)) * 0.5).astype(np.float32)
+    cs0 = rng.standard_normal((N, C, K - 1)).astype(np.float32)
+    out_ref, cs_ref = oracle.conv1d_silu_seq(x, w, cs0)
+    cs = dev(cs0)
+    out = torch.empty((N, T, C), device=DEV)
+    snaps = torch.full((N, T, C, K - 1), float("nan"), device=DEV)
+    gdn.gdn_conv1d_silu_seq_ex(dev(x), dev(w), cs, out, snaps)
+    assert_close(host(out), out_ref, "conv out")
+    assert np.array_equal(host(cs), cs_ref)
+    sn = host(snaps)
+    # history after position t = the last K-1 entries of (initial history ++ x[:t+1])
+    full = np.concatenate([cs0, np.transpose(x, (0, 2, 1))], axis=2)   # [N][C][K-1+T]
+    for t in range(T):
+        assert np.array_equal(sn[:, t], full[:, :, t + 1:t + K]), f"conv snapshot {t}"
