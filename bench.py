@@ -18,6 +18,9 @@ The same line carries the other workloads of the hot path ("legs"):
               (decay gate, sigmoid, L2 norm + GQA of q and k) before the
               recurrence
   decode_t4   the headline batch with the "T4" read-out (gdn_recurrence_ex)
+  prefill     one bf16 layer over 1 sequence x 4096 positions through
+              gdn_prefill_bf16 (fused conv/norm/gate front end, scan with the
+              16 -> 32 repeat by index, gated norm); tokens/s
   spec        a speculative-decoding verify step: 64 sequences x 4 draft
               tokens, 16 -> 32 heads by index, S = 128, conv over C = 8192,
               with per-token state and conv snapshots
@@ -60,7 +63,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="decode,scan,block,decode_full,decode_t4,spec")
+    ap.add_argument("--legs", default="decode,scan,block,decode_full,decode_t4,spec,prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
@@ -290,6 +293,38 @@ def run_spec(torch, gdn, inputs, steps, warmup):
             "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+def run_prefill(torch, gdn, inputs, steps, warmup):
+    d = inputs.draw_prefill()
+    N, T, H, S = d["z"].shape
+    HK, K = 16, d["conv_w"].shape[1]
+
+    def dev(x):
+        x = np.ascontiguousarray(x)
+        return torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).cuda()
+
+    t = {key: dev(val) for key, val in d.items()}
+    out = torch.empty((N, T, H, S), device="cuda")
+    ws = torch.empty(gdn.gdn_prefill_workspace_bytes(N, T, HK, H, S), dtype=torch.uint8,
+                     device="cuda")
+    scale = 1.0 / math.sqrt(S)
+    torch.cuda.synchronize()
+
+    def step():
+        gdn.gdn_prefill_bf16(t["qkv"], t["z"], t["a"], t["b"], t["conv_w"], t["A_log"],
+                             t["dt_bias"], t["norm_w"], t["conv_state"], t["state"], out, ws, HK,
+                             scale)
+
+    for _ in range(warmup):
+        step()
+    with Timer(torch) as tm:
+        for _ in range(steps):
+            step()
+    ms = tm.wall_ms / steps
+    return {"workload": "bf16 prefill of one layer: 1 sequence x 4096 positions, 16 -> 32 heads, "
+                        "S=128, C=8192, K=4",
+            "ms_per_step": ms, "tokens_per_s": N * T / (ms * 1e-3)}
+
+
 def block_layer_bytes(N, H, HK, S, K) -> int:
     C = 2 * HK * S + H * S
     return (2 * N * H * S * S * 4            # state read + write
@@ -444,6 +479,10 @@ def main():
     if "spec" in legs:
         log("leg spec: 64 seqs x 4 draft tokens with snapshots")
         out_legs["spec"] = run_spec(torch, gdn, inputs, K, W)
+        torch.cuda.empty_cache()
+    if "prefill" in legs:
+        log("leg prefill: bf16 layer, 4096 positions")
+        out_legs["prefill"] = run_prefill(torch, gdn, inputs, K, W)
         torch.cuda.empty_cache()
     if "scan" in legs:
         log("leg scan: conv 4096x8192 + recurrence T=4096")

@@ -39,6 +39,7 @@
 #ifndef GDN_H
 #define GDN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -240,6 +241,46 @@ int gdn_decode_block_bf16(const uint16_t *qkv, const uint16_t *z, const float *a
                           float *state, float *out, int n_seqs, int n_k_heads, int n_v_heads,
                           int state_size, int conv_kernel, float scale, float l2_eps, float eps,
                           void *stream);
+
+/*
+ * Workspace, in bytes, that gdn_prefill_bf16 needs for these sizes (0 for
+ * invalid sizes): normalised q and k per K-head, v, g, beta and y, fp32.
+ */
+size_t gdn_prefill_workspace_bytes(int n_seqs, int n_tokens, int n_k_heads, int n_v_heads,
+                                   int state_size);
+
+/*
+ * Prefill of one layer over n_tokens positions, bf16 activations, fp32 state:
+ * the decode layer of gdn_decode_block_bf16 chained over positions ([CU]'s
+ * batched "_nx" / "_seq" kernels: conv1d_silu_seq, qknorm_gqa_nx with the v
+ * pass-through, decay_gate_nx, recurrence_seq; then the gated norm).
+ *   1. conv1d + SiLU over the positions of the widened qkv (rolls
+ *      conv_state), split [q | k | v], q and k L2-normalised per K-head
+ *      (l2_eps), g = -exp(A_log)*softplus(a + dt_bias), beta = sigmoid(b);
+ *   2. the sequential scan, V-head vh reading K-head vh mod HK, y = scale *
+ *      (row . q);
+ *   3. out = gated RMSNorm(y, norm_w, widened z, eps).
+ * The result equals n_tokens calls of gdn_decode_block_bf16 bit for bit.
+ *   qkv        [n_seqs][n_tokens][C] bf16, C = 2*HK*S + H*S (8-byte aligned)
+ *   z          [n_seqs][n_tokens][n_v_heads][S] bf16 (8-byte aligned)
+ *   a, b       [n_seqs][n_tokens][n_v_heads]
+ *   conv_w [C][conv_kernel]; A_log, dt_bias [n_v_heads]; norm_w [S]
+ *   conv_state [n_seqs][C][conv_kernel-1], state [n_seqs][n_v_heads][S][S]
+ *              (both updated in place)
+ *   out        [n_seqs][n_tokens][n_v_heads][S]
+ *   workspace  caller-owned device memory of at least
+ *              gdn_prefill_workspace_bytes(...) bytes, 256-byte aligned; its
+ *              contents on return are unspecified
+ * Errors: GDN_ENULL; GDN_ESIZE (a shape <= 0, a count < 0, H not a multiple
+ * of HK, workspace too small); GDN_EUNSUPPORTED (S != 128, conv_kernel not in
+ * 2..4); GDN_EALIGN; GDN_ELAUNCH.
+ */
+int gdn_prefill_bf16(const uint16_t *qkv, const uint16_t *z, const float *a, const float *b,
+                     const float *conv_w, const float *A_log, const float *dt_bias,
+                     const float *norm_w, float *conv_state, float *state, float *out,
+                     void *workspace, size_t workspace_bytes, int n_seqs, int n_tokens,
+                     int n_k_heads, int n_v_heads, int state_size, int conv_kernel, float scale,
+                     float l2_eps, float eps, void *stream);
 
 #ifdef __cplusplus
 }

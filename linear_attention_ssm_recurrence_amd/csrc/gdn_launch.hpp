@@ -41,4 +41,9 @@ inline unsigned grid_for(int64_t items, int per_block) {
   return (unsigned)((items + per_block - 1) / per_block);
 }
 
+// Internal launchers shared between translation units (no argument checks:
+// the calling entry point has validated everything).
+int launch_gated_rmsnorm_bf16z(const float* y, const float* w, const uint16_t* z, float* out,
+                               int64_t n_rows, int head_dim, float eps, hipStream_t s);
+
 }  // namespace gdn

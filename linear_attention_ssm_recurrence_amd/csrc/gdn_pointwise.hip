@@ -63,9 +63,19 @@ __global__ __launch_bounds__(256) void l2norm_gqa_kernel(const float* __restrict
   }
 }
 
+__device__ __forceinline__ float4 load_z4(const float* z) { return load4(z); }
+
+__device__ __forceinline__ float4 load_z4(const uint16_t* z) {
+  const uint2 b = *reinterpret_cast<const uint2*>(z);
+  return make_float4(bf16_to_float((uint16_t)(b.x & 0xFFFFu)), bf16_to_float((uint16_t)(b.x >> 16)),
+                     bf16_to_float((uint16_t)(b.y & 0xFFFFu)), bf16_to_float((uint16_t)(b.y >> 16)));
+}
+
+// ZT is float, or uint16_t for a bf16 gate z (widened exactly on load).
+template <typename ZT>
 __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(const float* __restrict__ y,
                                                             const float* __restrict__ w,
-                                                            const float* __restrict__ z,
+                                                            const ZT* __restrict__ z,
                                                             float* __restrict__ out,
                                                             int64_t n_rows, int head_dim,
                                                             float eps) {
@@ -74,13 +84,13 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(const float* __restr
   if (row >= n_rows) return;  // uniform across the wave
   const int d4 = head_dim >> 2;
   const float* yr = y + row * head_dim;
-  const float* zr = z + row * head_dim;
+  const ZT* zr = z + row * head_dim;
   float* orow = out + row * head_dim;
   const float ss = row_sumsq(yr, d4, lane);
   const float inv = 1.0f / sqrtf(ss / (float)head_dim + eps);
   for (int m = lane; m < d4; m += 64) {
     const float4 yv = load4(yr + 4 * m);
-    const float4 zv = load4(zr + 4 * m);
+    const float4 zv = load_z4(zr + 4 * m);
     const float4 wv = load4(w + 4 * m);
     float4 o;
     o.x = yv.x * inv * wv.x * silu(zv.x);
@@ -143,7 +153,16 @@ extern "C" int gdn_gated_rmsnorm(const float* y, const float* w, const float* z,
   if (!y || !w || !z || !out) return GDN_ENULL;
   if (n_rows / 4 >= (int64_t(1) << 31)) return GDN_ESIZE;
   if (!aligned16(y) || !aligned16(w) || !aligned16(z) || !aligned16(out)) return GDN_EALIGN;
-  hipLaunchKernelGGL(gated_rmsnorm_kernel, dim3(grid_for(n_rows, 4)), dim3(256), 0,
+  hipLaunchKernelGGL(gated_rmsnorm_kernel<float>, dim3(grid_for(n_rows, 4)), dim3(256), 0,
                      as_stream(stream), y, w, z, out, n_rows, head_dim, eps);
   return launch_status();
 }
+
+namespace gdn {
+int launch_gated_rmsnorm_bf16z(const float* y, const float* w, const uint16_t* z, float* out,
+                               int64_t n_rows, int head_dim, float eps, hipStream_t s) {
+  hipLaunchKernelGGL(gated_rmsnorm_kernel<uint16_t>, dim3(grid_for(n_rows, 4)), dim3(256), 0, s,
+                     y, w, z, out, n_rows, head_dim, eps);
+  return launch_status();
+}
+}  // namespace gdn

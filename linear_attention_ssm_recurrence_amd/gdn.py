@@ -59,6 +59,7 @@ def load_library():
         "gdn_recurrence_seq": [P, P, P, P, P, P, P, I, I, I, I, F, P],
         "gdn_gated_rmsnorm": [P, P, P, P, L, I, F, P],
         "gdn_decode_block_bf16": [P] * 11 + [I] * 5 + [F] * 3 + [P],
+        "gdn_prefill_bf16": [P] * 12 + [ctypes.c_size_t] + [I] * 6 + [F] * 3 + [P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -67,6 +68,8 @@ def load_library():
     lib.gdn_strerror.argtypes = [I]
     lib.gdn_strerror.restype = ctypes.c_char_p
     lib.gdn_abi_version.restype = I
+    lib.gdn_prefill_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.gdn_prefill_workspace_bytes.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -74,7 +77,7 @@ def load_library():
 def header_symbols() -> list[str]:
     """Names of the entry points declared in include/gdn.h."""
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int)\s*(gdn_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int|size_t)\s*(gdn_\w+)\s*\(", text, re.M)))
 
 
 def strerror(code: int) -> str:
@@ -281,3 +284,36 @@ def _ptr16(t: torch.Tensor, what: str) -> int:
     if t.dtype not in (torch.int16, torch.bfloat16) and t.dtype != getattr(torch, "uint16", None):
         raise TypeError(f"{what} must hold bf16 bit patterns (int16/uint16/bfloat16), got {t.dtype}")
     return _ptr(t, t.dtype, what)
+
+
+def gdn_prefill_workspace_bytes(n_seqs, n_tokens, n_k_heads, n_v_heads, state_size) -> int:
+    return int(load_library().gdn_prefill_workspace_bytes(n_seqs, n_tokens, n_k_heads, n_v_heads,
+                                                          state_size))
+
+
+def gdn_prefill_bf16(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out,
+                     workspace, n_k_heads, scale, l2_eps=1e-6, eps=1e-6, stream=None):
+    """One layer over T positions. qkv [N][T][C] and z [N][T][H][S] hold bf16
+    bit patterns; a, b [N][T][H]; conv_w [C][K]; A_log, dt_bias [H]; norm_w [S];
+    conv_state [N][C][K-1] and state [N][H][S][S] updated in place;
+    out [N][T][H][S]; workspace a uint8 device tensor of at least
+    gdn_prefill_workspace_bytes(...) bytes."""
+    N, T, H, S = z.shape
+    C, K = conv_w.shape
+    _shape(qkv, (N, T, C), "qkv")
+    for t, nm in ((a, "a"), (b, "b")):
+        _shape(t, (N, T, H), nm)
+    _shape(A_log, (H,), "A_log")
+    _shape(dt_bias, (H,), "dt_bias")
+    _shape(norm_w, (S,), "norm_w")
+    _shape(conv_state, (N, C, K - 1), "conv_state")
+    _shape(state, (N, H, S, S), "state")
+    _shape(out, (N, T, H, S), "out")
+    if C != 2 * n_k_heads * S + H * S:
+        raise ValueError(f"conv_dim {C} != 2*n_k_heads*S + n_v_heads*S")
+    _call("gdn_prefill_bf16", _ptr16(qkv, "qkv"), _ptr16(z, "z"), _ptr(a, F32, "a"),
+          _ptr(b, F32, "b"), _ptr(conv_w, F32, "conv_w"), _ptr(A_log, F32, "A_log"),
+          _ptr(dt_bias, F32, "dt_bias"), _ptr(norm_w, F32, "norm_w"),
+          _ptr(conv_state, F32, "conv_state"), _ptr(state, F32, "state"), _ptr(out, F32, "out"),
+          _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), N, T, n_k_heads, H, S, K,
+          float(scale), float(l2_eps), float(eps), _stream(z, stream))

@@ -24,6 +24,10 @@ Workloads (H V-heads, HK K-heads, S state size, T tokens, N sequences):
                            + conv stage x [4096][8192], zero history
     4  decode block, bf16  N=64  48 layers, H=32 HK=16 S=128 C=8192 K=4,
                            layer l drawn from seed 4000 + l
+
+draw_prefill() draws one layer of a bf16 prefill over T positions with the
+decode block's distributions (the default seed and sizes: 1 sequence, 4096
+positions, 16 -> 32 heads, S=128, C=8192, K=4, zero initial state and history).
 """
 from __future__ import annotations
 
@@ -163,4 +167,30 @@ def draw_block_layer(layer: int, w: Workload | int = 4, n_seqs: int | None = Non
     d["qkv"] = to_bf16_bits(normal(rng, (N, C)))   # the conv input "x"
     d["norm_w"] = normal(rng, (S,), 0.1, 1.0)
     d["z"] = to_bf16_bits(normal(rng, (N, H, S)))
+    return d
+
+
+def draw_prefill(seed: int = 6, n_seqs: int = 1, n_tokens: int = 4096, n_k_heads: int = 16,
+                 n_v_heads: int = 32, state_size: int = 128, conv_kernel: int = 4,
+                 state_sigma: float = 0.0, conv_state_sigma: float = 0.0) -> dict:
+    """Raw draws for one prefill layer: qkv [N][T][C] and z [N][T][H][S] as bf16
+    bit patterns; a, b [N][T][H]; A_log, dt_bias (zeros) [H]; state
+    [N][H][S][S]; conv_w [C][K]; conv_state [N][C][K-1]; norm_w [S]. Drawn in
+    the module's order (a, b, A_log, state, conv_w, conv_state, x, norm_w, z)."""
+    N, T, HK, H, S, K = n_seqs, n_tokens, n_k_heads, n_v_heads, state_size, conv_kernel
+    C = 2 * HK * S + H * S
+    rng = np.random.default_rng(seed)
+    d = {}
+    d["a"] = normal(rng, (N, T, H))
+    d["b"] = normal(rng, (N, T, H))
+    d["A_log"] = normal(rng, (H,))
+    d["dt_bias"] = np.zeros((H,), dtype=np.float32)
+    d["state"] = (normal(rng, (N, H, S, S), state_sigma) if state_sigma > 0
+                  else np.zeros((N, H, S, S), dtype=np.float32))
+    d["conv_w"] = normal(rng, (C, K), 0.5)
+    d["conv_state"] = (normal(rng, (N, C, K - 1), conv_state_sigma) if conv_state_sigma > 0
+                       else np.zeros((N, C, K - 1), dtype=np.float32))
+    d["qkv"] = to_bf16_bits(normal(rng, (N, T, C)))
+    d["norm_w"] = normal(rng, (S,), 0.1, 1.0)
+    d["z"] = to_bf16_bits(normal(rng, (N, T, H, S)))
     return d

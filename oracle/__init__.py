@@ -65,10 +65,11 @@ def bind(path: str, prec: str):
     lib.oracle_recurrence_seq.argtypes = [P, P, P, P, P, P, P, I, I, I, I, real]
     lib.oracle_gated_rmsnorm.argtypes = [P, P, P, P, L, I, real]
     lib.oracle_decode_block_bf16.argtypes = [P] * 11 + [I] * 5 + [real] * 3
+    lib.oracle_prefill_bf16.argtypes = [P] * 11 + [I] * 6 + [real] * 3
     for name in ("oracle_decay_gate", "oracle_sigmoid", "oracle_l2norm_gqa",
                  "oracle_conv1d_silu_seq", "oracle_recurrence_seq",
                  "oracle_gated_rmsnorm", "oracle_decode_block_bf16",
-                 "oracle_set_threads"):
+                 "oracle_prefill_bf16", "oracle_set_threads"):
         getattr(lib, name).restype = None
     if lib.oracle_precision().decode() != prec:
         raise RuntimeError(f"{path} is not the {prec} build")
@@ -216,5 +217,30 @@ def decode_block_bf16(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state,
     _lib(prec).oracle_decode_block_bf16(
         _p(qkv), _p(z), _p(a), _p(b), _p(conv_w), _p(A_log), _p(dt_bias), _p(norm_w),
         _p(cs), _p(st), _p(out), N, n_k_heads, H, S, K,
+        float(scale), float(l2_eps), float(eps))
+    return out, cs, st
+
+
+def prefill_bf16(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, n_k_heads,
+                 scale, l2_eps=1e-6, eps=1e-6, prec="f32"):
+    """One layer over T positions with bf16 activations (uint16 bit patterns).
+
+    qkv [N][T][C] u16, z [N][T][H][S] u16, a, b [N][T][H], conv_w [C][K],
+    A_log, dt_bias [H], norm_w [S], conv_state [N][C][K-1], state [N][H][S][S]
+    -> (out [N][T][H][S], new_conv_state, new_state)
+    """
+    qkv = np.ascontiguousarray(qkv, dtype=np.uint16)
+    z = np.ascontiguousarray(z, dtype=np.uint16)
+    a, b = _arr(a, prec), _arr(b, prec)
+    conv_w, A_log, dt_bias, norm_w = (_arr(t, prec) for t in (conv_w, A_log, dt_bias, norm_w))
+    cs, st = _arr(conv_state, prec), _arr(state, prec)
+    N, T, H, S = z.shape
+    C, K = conv_w.shape
+    assert qkv.shape == (N, T, C) and C == 2 * n_k_heads * S + H * S
+    assert cs.shape == (N, C, K - 1) and st.shape == (N, H, S, S)
+    out = np.empty((N, T, H, S), dtype=_dtype(prec))
+    _lib(prec).oracle_prefill_bf16(
+        _p(qkv), _p(z), _p(a), _p(b), _p(conv_w), _p(A_log), _p(dt_bias), _p(norm_w),
+        _p(cs), _p(st), _p(out), N, T, n_k_heads, H, S, K,
         float(scale), float(l2_eps), float(eps))
     return out, cs, st

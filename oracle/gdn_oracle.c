@@ -379,3 +379,74 @@ void oracle_decode_block_bf16(const uint16_t *qkv, const uint16_t *z,
     free(yt);
     free(zt);
 }
+
+/* ------------------------------------------------------------------------
+ * Prefill of one layer over T positions, bf16 activations, fp32 state
+ *
+ * The decode layer above chained over positions, as [CU]'s batched kernels
+ * (conv1d_silu_seq, qknorm_gqa_nx with the v pass-through, decay_gate_nx,
+ * recurrence_seq) do it; the same stage functions, applied to all T
+ * positions of a sequence at once:
+ *   qkv [N][T][C] bf16, z [N][T][H][S] bf16, a, b [N][T][H],
+ *   conv_state [N][C][K-1], state [N][H][S][S], out [N][T][H][S]
+ * ------------------------------------------------------------------------ */
+void oracle_prefill_bf16(const uint16_t *qkv, const uint16_t *z, const real *a,
+                         const real *b, const real *conv_w, const real *A_log,
+                         const real *dt_bias, const real *norm_w,
+                         real *conv_state, real *state, real *out, int n_seqs,
+                         int n_tokens, int n_k_heads, int n_v_heads, int S,
+                         int K, real scale, real l2_eps, real eps)
+{
+    const int key_dim = n_k_heads * S;
+    const int val_dim = n_v_heads * S;
+    const int C = 2 * key_dim + val_dim;
+    const size_t T = (size_t)n_tokens;
+    real *x = (real *)malloc(sizeof(real) * T * C);
+    real *co = (real *)malloc(sizeof(real) * T * C);
+    real *qs = (real *)malloc(sizeof(real) * T * key_dim);
+    real *ks = (real *)malloc(sizeof(real) * T * key_dim);
+    real *qr = (real *)malloc(sizeof(real) * T * val_dim);
+    real *kr = (real *)malloc(sizeof(real) * T * val_dim);
+    real *vv = (real *)malloc(sizeof(real) * T * val_dim);
+    real *bt = (real *)malloc(sizeof(real) * T * n_v_heads);
+    real *gt = (real *)malloc(sizeof(real) * T * n_v_heads);
+    real *yt = (real *)malloc(sizeof(real) * T * val_dim);
+    real *zt = (real *)malloc(sizeof(real) * T * val_dim);
+
+    for (int n = 0; n < n_seqs; n++) {
+        for (size_t e = 0; e < T * C; e++)
+            x[e] = bf16_to_real(qkv[(size_t)n * T * C + e]);
+        oracle_conv1d_silu_seq(x, conv_w, conv_state + (size_t)n * C * (K - 1),
+                               co, 1, n_tokens, C, K);
+        for (size_t t = 0; t < T; t++) {
+            for (int e = 0; e < key_dim; e++) {
+                qs[t * key_dim + e] = co[t * C + e];
+                ks[t * key_dim + e] = co[t * C + key_dim + e];
+            }
+            for (int e = 0; e < val_dim; e++)
+                vv[t * val_dim + e] = co[t * C + 2 * key_dim + e];
+        }
+        oracle_l2norm_gqa(qs, qr, n_tokens, n_k_heads, n_v_heads, S, l2_eps);
+        oracle_l2norm_gqa(ks, kr, n_tokens, n_k_heads, n_v_heads, S, l2_eps);
+        oracle_sigmoid(b + (size_t)n * T * n_v_heads, bt, (long)(T * n_v_heads));
+        oracle_decay_gate(a + (size_t)n * T * n_v_heads, dt_bias, A_log, gt,
+                          n_v_heads, n_tokens);
+        oracle_recurrence_seq(state + (size_t)n * n_v_heads * S * S, qr, kr, vv,
+                              gt, bt, yt, 1, n_tokens, n_v_heads, S, scale);
+        for (size_t e = 0; e < T * val_dim; e++)
+            zt[e] = bf16_to_real(z[(size_t)n * T * val_dim + e]);
+        oracle_gated_rmsnorm(yt, norm_w, zt, out + (size_t)n * T * val_dim,
+                             (long)(T * n_v_heads), S, eps);
+    }
+    free(x);
+    free(co);
+    free(qs);
+    free(ks);
+    free(qr);
+    free(kr);
+    free(vv);
+    free(bt);
+    free(gt);
+    free(yt);
+    free(zt);
+}

@@ -488,4 +488,35 @@ def pin_block_is_composition(L32, L64):
         assert np.array_equal(st, st_ref)
 
 
+def _prefill_case(rng, N=2, T=6, HK=2, H=4, S=8, K=4):
+    from linear_attention_ssm_recurrence_amd import inputs
+    C = 2 * HK * S + H * S
+    bits = lambda x: inputs.to_bf16_bits(x.astype(np.float32))
+    return dict(qkv=bits(rng.standard_normal((N, T, C))), z=bits(rng.standard_normal((N, T, H, S))),
+                a=rng.standard_normal((N, T, H)), b=rng.standard_normal((N, T, H)),
+                conv_w=rng.standard_normal((C, K)) * 0.5, A_log=rng.standard_normal(H),
+                dt_bias=rng.standard_normal(H) * 0.1, norm_w=1 + 0.1 * rng.standard_normal(S),
+                conv_state=rng.standard_normal((N, C, K - 1)),
+                state=rng.standard_normal((N, H, S, S)) * 0.05, HK=HK, scale=1 / math.sqrt(S))
+
+
+def pin_prefill_is_chained_decode_layers(L32, L64):
+    """The prefill over T positions equals T single-position decode layers
+    chained (bitwise), so it composes the pinned stages the same way."""
+    rng = np.random.default_rng(31)
+    c = _prefill_case(rng)
+    for L in (L32, L64):
+        out, cs, st = oracle.prefill_bf16(c["qkv"], c["z"], c["a"], c["b"], c["conv_w"], c["A_log"],
+                                          c["dt_bias"], c["norm_w"], c["conv_state"], c["state"],
+                                          c["HK"], c["scale"], prec=L)
+        cs2, st2 = c["conv_state"], c["state"]
+        T = c["qkv"].shape[1]
+        for t in range(T):
+            o, cs2, st2 = oracle.decode_block_bf16(
+                c["qkv"][:, t], c["z"][:, t], c["a"][:, t], c["b"][:, t], c["conv_w"], c["A_log"],
+                c["dt_bias"], c["norm_w"], cs2, st2, c["HK"], c["scale"], prec=L)
+            assert np.array_equal(o, out[:, t]), f"position {t}"
+        assert np.array_equal(cs2, cs) and np.array_equal(st2, st)
+
+
 ALL_PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

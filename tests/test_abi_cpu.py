@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_header_symbol(lib):
     names = gdn.header_symbols()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     out = os.popen(f"nm -D --defined-only {gdn.LIB_PATH}").read()
     exported = set(re.findall(r"\sT\s(gdn_\w+)", out))
     for name in names:
@@ -158,6 +158,27 @@ def test_block_validation(lib):
     assert call(state=FAKE_MIS) == gdn.GDN_EALIGN
     assert call(z=ctypes.c_void_p(0x10002)) == gdn.GDN_EALIGN
     assert call(first=NUL, state=NUL, n=0) == gdn.GDN_OK
+
+
+def test_prefill_validation(lib):
+    f = lib.gdn_prefill_bf16
+    need = lib.gdn_prefill_workspace_bytes(1, 8, 2, 4, 128)
+    assert need > 0
+    assert lib.gdn_prefill_workspace_bytes(1, 8, 2, 4, 0) == 0
+
+    def call(first=FAKE, ws=FAKE, ws_bytes=need, n=1, T=8, HK=2, H=4, S=128, K=4):
+        return f(first, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, ws_bytes,
+                 n, T, HK, H, S, K, 0.1, 1e-6, 1e-6, NUL)
+
+    assert call(first=NUL) == gdn.GDN_ENULL
+    assert call(ws=NUL) == gdn.GDN_ENULL
+    assert call(ws_bytes=need - 1) == gdn.GDN_ESIZE
+    assert call(ws=ctypes.c_void_p(0x10010)) == gdn.GDN_EALIGN
+    assert call(HK=3) == gdn.GDN_ESIZE
+    assert call(S=64) == gdn.GDN_EUNSUPPORTED
+    assert call(K=1) == gdn.GDN_EUNSUPPORTED
+    assert call(T=-1) == gdn.GDN_ESIZE
+    assert call(first=NUL, ws=NUL, T=0) == gdn.GDN_OK
 
 
 def test_python_binding_rejects_cpu_tensors(lib):

@@ -78,6 +78,10 @@ MUTANTS = {
         "for (int vh = kh * (n_v_heads / n_k_heads); vh < (kh + 1) * (n_v_heads / n_k_heads); vh++) {"),
     "block_v_offset": ("co + 2 * key_dim, gt, bt, yt", "co + key_dim, gt, bt, yt"),
     "block_k_from_q": ("oracle_l2norm_gqa(co + key_dim, kr,", "oracle_l2norm_gqa(co, kr,"),
+    "prefill_k_split": ("ks[t * key_dim + e] = co[t * C + key_dim + e];",
+                        "ks[t * key_dim + e] = co[t * C + e];"),
+    "prefill_gate_rows": ("gt,\n                          n_v_heads, n_tokens);",
+                          "gt,\n                          n_v_heads, 1);"),
 }
 
 
