@@ -216,6 +216,11 @@ def run_scan(torch, gdn, inputs, steps, warmup):
     def scan():
         gdn.gdn_recurrence_seq(st, q, k, v, g, beta, y, w.scale)
 
+    ws = torch.empty(gdn.gdn_chunked_workspace_bytes(N, T, H, S), dtype=torch.uint8, device="cuda")
+
+    def chunked():
+        gdn.gdn_recurrence_seq_chunked(st, q, k, v, g, beta, y, w.scale, ws)
+
     for _ in range(warmup):
         conv()
         scan()
@@ -229,6 +234,11 @@ def run_scan(torch, gdn, inputs, steps, warmup):
     with Timer(torch) as t_scan:
         for _ in range(steps):
             scan()
+    for _ in range(warmup):
+        chunked()
+    with Timer(torch) as t_chunk:
+        for _ in range(steps):
+            chunked()
     ms = t_all.wall_ms / steps
     scan_ms = t_scan.event_ms / steps
     conv_ms = t_conv.event_ms / steps
@@ -245,6 +255,8 @@ def run_scan(torch, gdn, inputs, steps, warmup):
         "scan_TFLOPs": flops / (scan_ms * 1e-3) / 1e12,
         "scan_frac_fp32_vector_peak": flops / (scan_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
         "scan_algorithmic_bytes": scan_bytes,
+        "chunked_scan_ms": t_chunk.event_ms / steps,
+        "chunked_scan_tokens_per_s": N * T / (t_chunk.event_ms / steps * 1e-3),
         "conv_kernel_ms": conv_ms,
         "conv_GBps": conv_bytes / (conv_ms * 1e-3) / 1e9,
         "conv_frac_hbm_peak": conv_bytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,

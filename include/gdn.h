@@ -282,6 +282,32 @@ int gdn_prefill_bf16(const uint16_t *qkv, const uint16_t *z, const float *a, con
                      int n_k_heads, int n_v_heads, int state_size, int conv_kernel, float scale,
                      float l2_eps, float eps, void *stream);
 
+/*
+ * Workspace, in bytes, that gdn_recurrence_seq_chunked needs (0 for invalid
+ * sizes or an unsupported state size): per (sequence, V-head, 64-position
+ * chunk) 16448 floats.
+ */
+size_t gdn_chunked_workspace_bytes(int n_seqs, int n_tokens, int n_v_heads, int state_size);
+
+/*
+ * The scan of gdn_recurrence_seq_ex (no snapshots) in chunked form: the
+ * positions are taken 64 at a time and the delta rule over a chunk is applied
+ * as matrix products (WY-style blocking, fp32 MFMA). The pages name a chunked
+ * prefill and keep the sequential scan as its reference ([FM] "softplus"
+ * comment and the sequential-scan section) without giving its algorithm.
+ * Same arguments and layouts as gdn_recurrence_seq_ex, plus a caller-owned
+ * workspace of at least gdn_chunked_workspace_bytes(...) bytes (16-byte
+ * aligned; contents on return unspecified). y and the state agree with the
+ * sequential scan within the fp32 tolerance, not bit for bit.
+ * Errors: GDN_ENULL; GDN_ESIZE (as gdn_recurrence_seq_ex, or workspace too
+ * small); GDN_EUNSUPPORTED (state_size != 128); GDN_EALIGN (state, q, k, v or
+ * workspace not 16-byte aligned); GDN_ELAUNCH.
+ */
+int gdn_recurrence_seq_chunked(float *state, const float *q, const float *k, const float *v,
+                               const float *g, const float *beta, float *y, void *workspace,
+                               size_t workspace_bytes, int n_seqs, int n_tokens, int n_k_heads,
+                               int n_v_heads, int state_size, float scale, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

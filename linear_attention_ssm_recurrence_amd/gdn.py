@@ -60,6 +60,7 @@ def load_library():
         "gdn_gated_rmsnorm": [P, P, P, P, L, I, F, P],
         "gdn_decode_block_bf16": [P] * 11 + [I] * 5 + [F] * 3 + [P],
         "gdn_prefill_bf16": [P] * 12 + [ctypes.c_size_t] + [I] * 6 + [F] * 3 + [P],
+        "gdn_recurrence_seq_chunked": [P] * 8 + [ctypes.c_size_t] + [I] * 5 + [F, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -70,6 +71,8 @@ def load_library():
     lib.gdn_abi_version.restype = I
     lib.gdn_prefill_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.gdn_prefill_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_chunked_workspace_bytes.argtypes = [I, I, I, I]
+    lib.gdn_chunked_workspace_bytes.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -317,3 +320,25 @@ def gdn_prefill_bf16(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, s
           _ptr(conv_state, F32, "conv_state"), _ptr(state, F32, "state"), _ptr(out, F32, "out"),
           _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), N, T, n_k_heads, H, S, K,
           float(scale), float(l2_eps), float(eps), _stream(z, stream))
+
+
+def gdn_chunked_workspace_bytes(n_seqs, n_tokens, n_v_heads, state_size) -> int:
+    return int(load_library().gdn_chunked_workspace_bytes(n_seqs, n_tokens, n_v_heads, state_size))
+
+
+def gdn_recurrence_seq_chunked(state, q, k, v, g, beta, y, scale, workspace, stream=None):
+    """Chunked scan. state [N][H][S][S] in place; q, k [N][T][HK][S];
+    v, y [N][T][H][S]; g, beta [N][T][H]; workspace a uint8 device tensor of
+    at least gdn_chunked_workspace_bytes(N, T, H, S) bytes."""
+    N, T, H, S = v.shape
+    HK = q.shape[2]
+    _shape(state, (N, H, S, S), "state")
+    _shape(q, (N, T, HK, S), "q")
+    _shape(k, (N, T, HK, S), "k")
+    _shape(y, (N, T, H, S), "y")
+    _shape(g, (N, T, H), "g")
+    _shape(beta, (N, T, H), "beta")
+    _call("gdn_recurrence_seq_chunked", _ptr(state, F32, "state"), _ptr(q, F32, "q"),
+          _ptr(k, F32, "k"), _ptr(v, F32, "v"), _ptr(g, F32, "g"), _ptr(beta, F32, "beta"),
+          _ptr(y, F32, "y"), _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+          N, T, HK, H, S, float(scale), _stream(v, stream))

@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_header_symbol(lib):
     names = gdn.header_symbols()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     out = os.popen(f"nm -D --defined-only {gdn.LIB_PATH}").read()
     exported = set(re.findall(r"\sT\s(gdn_\w+)", out))
     for name in names:
@@ -179,6 +179,25 @@ def test_prefill_validation(lib):
     assert call(K=1) == gdn.GDN_EUNSUPPORTED
     assert call(T=-1) == gdn.GDN_ESIZE
     assert call(first=NUL, ws=NUL, T=0) == gdn.GDN_OK
+
+
+def test_chunked_validation(lib):
+    f = lib.gdn_recurrence_seq_chunked
+    need = lib.gdn_chunked_workspace_bytes(1, 100, 4, 128)
+    assert need == 1 * 4 * 2 * 16448 * 4
+    assert lib.gdn_chunked_workspace_bytes(1, 100, 4, 64) == 0
+
+    def call(state=FAKE, ws=FAKE, ws_bytes=need, T=100, HK=2, H=4, S=128):
+        return f(state, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, ws_bytes, 1, T, HK, H, S, 0.1, NUL)
+
+    assert call(state=NUL) == gdn.GDN_ENULL
+    assert call(ws=NUL) == gdn.GDN_ENULL
+    assert call(ws_bytes=need - 4) == gdn.GDN_ESIZE
+    assert call(S=64) == gdn.GDN_EUNSUPPORTED
+    assert call(HK=3) == gdn.GDN_ESIZE
+    assert call(state=FAKE_MIS) == gdn.GDN_EALIGN
+    assert call(ws=FAKE_MIS) == gdn.GDN_EALIGN
+    assert call(state=NUL, ws=NUL, T=0) == gdn.GDN_OK
 
 
 def test_python_binding_rejects_cpu_tensors(lib):

@@ -1,0 +1,80 @@
+"""Parity of the chunked scan (gdn_recurrence_seq_chunked) with the oracle's
+sequential scan, within the fp32 tolerance (needs an MI355X)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (DEV, RTOL_LONG_SCAN, assert_close, dev, host, oracle_threads,
+                         prep_recurrence)
+from linear_attention_ssm_recurrence_amd import gdn, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdn.load_library()
+    oracle_threads()
+
+
+def _case(rng, N, T, HK, H, S=128, state_sigma=0.05, a_log_shift=0.0):
+    qh = oracle.l2norm_gqa(rng.standard_normal((N, T, HK, S)), HK)
+    kh = oracle.l2norm_gqa(rng.standard_normal((N, T, HK, S)), HK)
+    rep = lambda x: np.ascontiguousarray(x[:, :, np.arange(H) % HK, :])
+    v = rng.standard_normal((N, T, H, S)).astype(np.float32)
+    g = oracle.decay_gate(rng.standard_normal((N, T, H)), np.zeros(H),
+                          rng.standard_normal(H) + a_log_shift)
+    beta = oracle.sigmoid(rng.standard_normal((N, T, H)))
+    st = (rng.standard_normal((N, H, S, S)) * state_sigma).astype(np.float32)
+    return dict(qh=qh, kh=kh, q=rep(qh), k=rep(kh), v=v, g=g, beta=beta, state=st)
+
+
+def _gpu_chunked(p, scale):
+    N, T, H, S = p["v"].shape
+    st = dev(p["state"])
+    y = torch.empty((N, T, H, S), device=DEV)
+    ws = torch.empty(gdn.gdn_chunked_workspace_bytes(N, T, H, S), dtype=torch.uint8, device=DEV)
+    gdn.gdn_recurrence_seq_chunked(st, dev(p["qh"]), dev(p["kh"]), dev(p["v"]), dev(p["g"]),
+                                   dev(p["beta"]), y, scale, ws)
+    return y, st
+
+
+@pytest.mark.parametrize("N,T,HK,H", [(1, 1, 2, 2), (1, 63, 2, 2), (1, 64, 2, 2),
+                                       (2, 65, 2, 4), (1, 200, 1, 2), (3, 130, 4, 8)])
+def test_chunked_vs_oracle(N, T, HK, H):
+    rng = np.random.default_rng(800 + T + N)
+    p = _case(rng, N, T, HK, H)
+    scale = 1 / math.sqrt(128)
+    y_ref, st_ref = oracle.recurrence_seq(p["state"], p["q"], p["k"], p["v"], p["g"], p["beta"], scale)
+    y, st = _gpu_chunked(p, scale)
+    assert_close(host(y), y_ref, f"chunked y N={N} T={T}")
+    assert_close(host(st), st_ref, f"chunked state N={N} T={T}")
+
+
+def test_chunked_strong_decay():
+    """Heads whose decay underflows within a chunk (A_log shifted up by 4)."""
+    rng = np.random.default_rng(77)
+    p = _case(rng, 1, 150, 2, 4, a_log_shift=4.0)
+    assert p["g"].min() < -50
+    scale = 1 / math.sqrt(128)
+    y_ref, st_ref = oracle.recurrence_seq(p["state"], p["q"], p["k"], p["v"], p["g"], p["beta"], scale)
+    y, st = _gpu_chunked(p, scale)
+    assert_close(host(y), y_ref, "chunked y, strong decay")
+    assert_close(host(st), st_ref, "chunked state, strong decay")
+
+
+def test_chunked_scan_4096():
+    """1 sequence x 4096 tokens x 32 heads x S = 128, zero initial state."""
+    w = inputs.WORKLOADS[3]
+    d = inputs.draw(w, with_conv=False)
+    p = prep_recurrence(d, w)
+    p["qh"], p["kh"] = p["q"], p["k"]          # HK = H for this workload
+    y_ref, st_ref = oracle.recurrence_seq(p["state"], p["q"], p["k"], p["v"], p["g"], p["beta"], w.scale)
+    y, st = _gpu_chunked(p, w.scale)
+    assert_close(host(y), y_ref, "chunked y T=4096", rtol=RTOL_LONG_SCAN)
+    assert_close(host(st), st_ref, "chunked state T=4096", rtol=RTOL_LONG_SCAN)
