@@ -18,14 +18,18 @@
 // Two kernels:
 //  chunk_prep_kernel  one block per (sequence, V-head, chunk), all chunks in
 //                     parallel: Gc, then K K^T and Q K^T (lower tiles, MFMA),
-//                     A and P, X by forward substitution (4 lanes per column),
-//                     W (MFMA). Writes Gc, Tt, P, W to the workspace.
+//                     A and P, X blockwise (16 x 16 diagonal tiles by forward
+//                     substitution, the others by MFMA), W (MFMA). Writes
+//                     gamma, gamma_C/gamma, Tt, P, W to the workspace. Gc is
+//                     summed in fp64: with strong decay it reaches thousands,
+//                     where an fp32 difference Gc_t - Gc_s would lose ~1e-4.
 //  chunk_scan_kernel  one block per (sequence, V-head, 16 state rows), the
 //                     chunks in order: the 16 rows stay on chip, and per chunk
 //                     each of the 4 waves does 128 MFMAs (U, Y, state update).
 // Positions past the end of the sequence in the last chunk are padded with
-// g = 0, beta = 0 and k = q = 0: their rows of A, W and U are zero, so they
-// leave the state unchanged, and their y are not stored.
+// g = 0, beta = 0 and k = q = 0 in the preparation: their rows of A, Tt, W
+// and U and their columns of Tt are zero, so they leave the state unchanged,
+// and their y are not stored.
 //
 // MFMA v_mfma_f32_16x16x4f32 (checked on MI355X): lane l supplies
 // A[l%16][l/16] and B[l/16][l%16]; output element i of lane l is
@@ -44,14 +48,15 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 constexpr int kChS = 128;     // state size
 constexpr int kChC = 64;      // chunk length
 constexpr int kChR = 16;      // state rows per scan block
-constexpr int kChUnit = kChC + 2 * kChC * kChC + kChC * kChS;  // floats per (seq, head, chunk)
+constexpr int kChUnit = 2 * kChC + 2 * kChC * kChC + kChC * kChS;  // floats per (seq, head, chunk)
 
 __device__ __forceinline__ f32x4v mfma4(float a, float b, f32x4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 struct ChunkUnit {   // views into one unit of the workspace
-  float* gc;  // [C]
+  float* gam; // [C]      gamma_t = exp(Gc_t)
+  float* ktf; // [C]      gamma_C / gamma_s
   float* tt;  // [C][C]   X diag(beta)
   float* p;   // [C][C]   (gamma_t/gamma_s) q_t.k_s, s <= t
   float* w;   // [C][S]   X diag(beta gamma) K
@@ -59,7 +64,8 @@ struct ChunkUnit {   // views into one unit of the workspace
 
 __device__ __forceinline__ ChunkUnit chunk_unit(float* ws, int64_t unit) {
   float* base = ws + unit * kChUnit;
-  return {base, base + kChC, base + kChC + kChC * kChC, base + kChC + 2 * kChC * kChC};
+  float* mats = base + 2 * kChC;
+  return {base, base + kChC, mats, mats + kChC * kChC, mats + 2 * kChC * kChC};
 }
 
 // ---------------------------------------------------------------------------
@@ -67,18 +73,22 @@ __device__ __forceinline__ ChunkUnit chunk_unit(float* ws, int64_t unit) {
 // ---------------------------------------------------------------------------
 constexpr int kKP = kChS + 4;   // LDS row pitch of K and Q (floats)
 constexpr int kAP = kChC + 4;   // LDS row pitch of A and X
+constexpr int kTP = 16 + 4;     // LDS row pitch of a 16 x 16 scratch tile
 
 __global__ __launch_bounds__(256) void chunk_prep_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, float* __restrict__ ws, int n_tokens, int n_k_heads,
     int n_v_heads, int n_chunks) {
   constexpr int S = kChS, C = kChC;
-  constexpr int QS = (C * kKP > 2 * C * kAP) ? C * kKP : 2 * C * kAP;
+  constexpr int AXT = 2 * C * kAP + 3 * 16 * kTP;   // A, X and three scratch tiles
+  constexpr int QS = (C * kKP > AXT) ? C * kKP : AXT;
   __shared__ float Ks[C * kKP];
   __shared__ float Qs[QS];        // reused for A and X once Q K^T is done
-  __shared__ float Gs[C], Bs[C], BG[C];
+  __shared__ double Gs[C];        // Gc in fp64: differences of large sums keep their precision
+  __shared__ float Bs[C], BG[C];
   float* As = Qs;                 // [C][kAP]
   float* Xs = Qs + C * kAP;       // [C][kAP]
+  float* Ts = Qs + 2 * C * kAP;   // [3][16][kTP]
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t unit = blockIdx.x;                    // (n * H + h) * n_chunks + c
@@ -104,26 +114,26 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     store4(Ks + t * kKP + col, kv);
     store4(Qs + t * kKP + col, qv);
   }
-  // cumulative log-decay and beta (wave 0; sequential prefix sum by lane 0)
+  // cumulative log-decay (inclusive prefix sum across wave 0) and beta
   if (wv == 0) {
     const int t = t0 + lane;
     const bool ok = t < n_tokens;
     const int64_t gi = (n * n_tokens + t) * n_v_heads + h;
-    Gs[lane] = ok ? g[gi] : 0.0f;
+    double gc = ok ? (double)g[gi] : 0.0;
+#pragma unroll
+    for (int off = 1; off < C; off <<= 1) {
+      const double up = __shfl_up(gc, off);
+      gc = lane >= off ? gc + up : gc;
+    }
+    Gs[lane] = gc;
     Bs[lane] = ok ? beta[gi] : 0.0f;
   }
   __syncthreads();
-  if (tid == 0) {
-    float acc = 0.0f;
-    for (int t = 0; t < C; ++t) {
-      acc += Gs[t];
-      Gs[t] = acc;
-    }
-  }
-  __syncthreads();
   if (tid < C) {
-    u.gc[tid] = Gs[tid];
-    BG[tid] = Bs[tid] * expf(Gs[tid]);   // beta_s gamma_s
+    const float gam = expf((float)Gs[tid]);
+    u.gam[tid] = gam;
+    u.ktf[tid] = expf((float)(Gs[C - 1] - Gs[tid]));
+    BG[tid] = Bs[tid] * gam;             // beta_s gamma_s
   }
 
   // K K^T and Q K^T on the lower tiles (ti >= tj): 10 tiles each, 20 per
@@ -166,7 +176,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = ti * 16 + g4 * 4 + i, s = tj * 16 + l16;
-      const float r = expf(Gs[t] - Gs[s]);
+      const float r = expf((float)(Gs[t] - Gs[s]));
       if (idx < 10) {
         As[t * kAP + s] = (s < t) ? Bs[t] * r * acc5[m][i] : 0.0f;
       } else {
@@ -181,17 +191,60 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
   }
   __syncthreads();
 
-  // X = (I + A)^-1, column by column; four lanes per column split the sum
+  // X = (I + A)^-1 blockwise on 16 x 16 tiles. Diagonal tiles: wave w
+  // inverts tile (w, w) by forward substitution, one column per lane (the
+  // four 16-lane groups compute the same columns; group 0 stores them).
   {
-    const int col = tid >> 2, part = tid & 3;
-    for (int t = 0; t < C; ++t) {
+    const int b = wv, col = l16;
+    float xr[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const float* arow = As + (16 * b + t) * kAP + 16 * b;
       float acc = 0.0f;
-      for (int s = part; s < t; s += 4) acc = __builtin_fmaf(As[t * kAP + s], Xs[s * kAP + col], acc);
-      acc = acc + dpp_mov<kDppQuadXor1>(acc);
-      acc = acc + dpp_mov<kDppQuadXor2>(acc);
-      if (part == 0) Xs[t * kAP + col] = (t == col ? 1.0f : 0.0f) - acc;
-      __syncthreads();
+#pragma unroll
+      for (int s2 = 0; s2 < t; ++s2) acc = __builtin_fmaf(arow[s2], xr[s2], acc);
+      xr[t] = (t == col ? 1.0f : 0.0f) - acc;
     }
+    if (g4 == 0) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) Xs[(16 * b + t) * kAP + 16 * b + col] = xr[t];
+    }
+    for (int f = tid; f < C * C; f += 256) {   // X is lower block-triangular
+      const int t = f / C, s2 = f % C;
+      if ((s2 >> 4) > (t >> 4)) Xs[t * kAP + s2] = 0.0f;
+    }
+  }
+  __syncthreads();
+  // Off-diagonal tiles, one block row at a time:
+  //   X_ij = -X_ii (sum_{j <= m < i} A_im X_mj),   wave j computes tile (i, j)
+  for (int bi = 1; bi < 4; ++bi) {
+    const int bj = wv;
+    if (bj < bi) {
+      f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+      for (int bm = bj; bm < bi; ++bm) {
+        const float4 a4 = load4(As + (16 * bi + l16) * kAP + 16 * bm + 4 * g4);
+        const float* xb = Xs + (16 * bm + 4 * g4) * kAP + 16 * bj + l16;
+        acc = mfma4(a4.x, xb[0 * kAP], acc);
+        acc = mfma4(a4.y, xb[1 * kAP], acc);
+        acc = mfma4(a4.z, xb[2 * kAP], acc);
+        acc = mfma4(a4.w, xb[3 * kAP], acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Ts[(bj * 16 + 4 * g4 + i) * kTP + l16] = acc[i];
+    }
+    __syncthreads();
+    if (bj < bi) {
+      const float4 x4 = load4(Xs + (16 * bi + l16) * kAP + 16 * bi + 4 * g4);
+      const float* tb = Ts + (bj * 16 + 4 * g4) * kTP + l16;
+      f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma4(x4.x, tb[0 * kTP], acc);
+      acc = mfma4(x4.y, tb[1 * kTP], acc);
+      acc = mfma4(x4.z, tb[2 * kTP], acc);
+      acc = mfma4(x4.w, tb[3 * kTP], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Xs[(16 * bi + 4 * g4 + i) * kAP + 16 * bj + l16] = -acc[i];
+    }
+    __syncthreads();
   }
   // Tt = X diag(beta)
   for (int f = tid; f < C * C; f += 256) {
@@ -219,8 +272,19 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kMP = kChS + 4;   // LDS pitch of the state rows
 constexpr int kUP = kChR + 4;   // LDS pitch of U and V
+constexpr int kKSP = kChS + 4;  // LDS pitch of the chunk's K
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
+// What one chunk needs from memory, per lane: the A-operand rows of Tt and P
+// (16 floats each), W and q (32 each) for the lane's position row, and this
+// thread's share of K (8 float4) and V (1 float4) for LDS staging. Each group
+// is refilled with the next chunk's values right after its last use, so the
+// loads overlap the rest of the chunk.
+struct ChunkRegs {
+  float4 tt[4], p[4], w[8], q[8], kst[8], v;
+  float gam, ktf;
+};
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
                        const float* __restrict__ k, const float* __restrict__ v,
                        const float* __restrict__ ws, float* __restrict__ y, int n_tokens,
@@ -229,13 +293,16 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
   __shared__ float Ms[R * kMP];
   __shared__ float Us[C * kUP];
   __shared__ float Vs[C * kUP];
-  __shared__ float Gam[C];   // gamma_t = exp(Gc_t)
-  __shared__ float Ktf[C];   // gamma_C / gamma_s = exp(Gc_C - Gc_s)
+  __shared__ float Ks[C * kKSP];
+  __shared__ float Gam[C];   // gamma_t
+  __shared__ float Ktf[C];   // gamma_C / gamma_s
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
-  const int64_t head = blockIdx.x / (S / R);          // n * H + h
-  const int row0 = (int)(blockIdx.x % (S / R)) * R;
+  // the S/R blocks of one head read the same operands: keep them on one XCD
+  const unsigned blk = xcd_group(blockIdx.x, gridDim.x);
+  const int64_t head = blk / (S / R);                 // n * H + h
+  const int row0 = (int)(blk % (S / R)) * R;
   const int64_t n = head / n_v_heads;
   const int h = (int)(head % n_v_heads);
   const int kh = h % n_k_heads;
@@ -245,109 +312,140 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
   const float* vn = v + (n * n_tokens) * v_tok + (int64_t)h * S + row0;
   float* yn = y + (n * n_tokens) * v_tok + (int64_t)h * S + row0;
   float* sp = state + head * (int64_t)S * S + (int64_t)row0 * S;
+  const int trow = wv * 16 + l16;                     // this lane's A-operand row
+  const int last_tok = n_tokens - 1;
+  // Positions past the end read the last valid row instead, unzeroed: the
+  // workspace operands are exactly zero there (beta = 0 makes those rows of
+  // Tt, W and U, and those columns of Tt, zero), so K and V rows meet only
+  // zeros, and q rows only reach y rows that are not stored. (Zeroing on
+  // load would make the compiler wait for each prefetch as it is issued.)
+  auto tok_clamp = [&](int t) { return t < last_tok ? t : last_tok; };
 
-  // state rows: LDS copy (B operand of M^T products) and this wave's two
-  // 16 x 16 column tiles in the MFMA output layout (the update accumulators)
-  for (int f = tid * 4; f < R * S; f += 256 * 4) store4(Ms + (f / S) * kMP + f % S, load4(sp + f));
+  auto unit_of = [&](int chunk) {
+    return chunk_unit(const_cast<float*>(ws), head * n_chunks + chunk);
+  };
+  auto fetch_kv = [&](int chunk, ChunkRegs& f) {   // K, V, decay factors: staged through LDS
+    const int t0 = chunk * C;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int fi = (j * 256 + tid) * 4, t = fi / S, col = fi % S;
+      f.kst[j] = load4(kn + (int64_t)tok_clamp(t0 + t) * kq_tok + col);
+    }
+    const int t = tid >> 2;
+    f.v = load4(vn + (int64_t)tok_clamp(t0 + t) * v_tok + (tid & 3) * 4);
+    const ChunkUnit u = unit_of(chunk);
+    f.gam = (wv == 0) ? u.gam[lane] : 0.0f;
+    f.ktf = (wv == 0) ? u.ktf[lane] : 0.0f;
+  };
+  auto fetch_a = [&](int chunk, ChunkRegs& f) {    // Tt, W, q rows
+    const ChunkUnit u = unit_of(chunk);
+    const int t = chunk * C + trow;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.tt[j] = load4(u.tt + trow * C + g4 * (C / 4) + 4 * j);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      f.w[j] = load4(u.w + trow * S + g4 * (S / 4) + 4 * j);
+      f.q[j] = load4(qn + (int64_t)tok_clamp(t) * kq_tok + g4 * (S / 4) + 4 * j);
+    }
+  };
+  auto fetch_p = [&](int chunk, ChunkRegs& f) {    // P rows
+    const ChunkUnit u = unit_of(chunk);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.p[j] = load4(u.p + trow * C + g4 * (C / 4) + 4 * j);
+  };
+
+  // state rows: LDS copy (B operand of the M^T products) and this wave's two
+  // 16 x 16 column tiles in the MFMA output layout (the update accumulators),
+  // taken from the LDS copy so that no global load is pending in the loop
+  for (int fi = tid * 4; fi < R * S; fi += 256 * 4)
+    store4(Ms + (fi / S) * kMP + fi % S, load4(sp + fi));
+  __syncthreads();
   f32x4v macc[2];
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) macc[c2][i] = sp[(g4 * 4 + i) * S + (wv * 2 + c2) * 16 + l16];
+    for (int i = 0; i < 4; ++i) macc[c2][i] = Ms[(g4 * 4 + i) * kMP + (wv * 2 + c2) * 16 + l16];
+
+  ChunkRegs f;
+  fetch_kv(0, f);
+  fetch_a(0, f);
+  fetch_p(0, f);
 
   for (int chunk = 0; chunk < n_chunks; ++chunk) {
     const int t0 = chunk * C;
-    const ChunkUnit u = chunk_unit(const_cast<float*>(ws), head * n_chunks + chunk);
-    // V of the block's rows (zero past the end), and Gc
-    {
-      const int t = tid >> 2, c4 = (tid & 3) * 4;
-      float4 vv = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (t0 + t < n_tokens) vv = load4(vn + (int64_t)(t0 + t) * v_tok + c4);
-      store4(Vs + t * kUP + c4, vv);
-      if (tid < C) {
-        const float gc = u.gc[tid];
-        Gam[tid] = expf(gc);
-        Ktf[tid] = expf(u.gc[C - 1] - gc);
-      }
+    const int nx = chunk + 1 < n_chunks ? chunk + 1 : chunk;   // last chunk: harmless re-read
+    // stage K, V and the decay factors, then start the next chunk's K, V, Gc
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int fi = (j * 256 + tid) * 4;
+      store4(Ks + (fi / S) * kKSP + fi % S, f.kst[j]);
     }
+    store4(Vs + (tid >> 2) * kUP + (tid & 3) * 4, f.v);
+    if (wv == 0) {
+      Gam[lane] = f.gam;
+      Ktf[lane] = f.ktf;
+    }
+    fetch_kv(nx, f);
     __syncthreads();
 
-    // U rows 16wv..16wv+15 = Tt V - W M^T ; Y part = gamma Q M^T
-    const int trow = wv * 16 + l16;                   // this lane's A-operand row
-    const bool tok_ok = t0 + trow < n_tokens;
+    // U rows 16wv..16wv+15 = Tt V - W M^T ; y part 1 = gamma Q M^T
     f32x4v uacc = {0.f, 0.f, 0.f, 0.f}, yacc = {0.f, 0.f, 0.f, 0.f};
-    {
-      const float* ttr = u.tt + trow * C + g4 * (C / 4);
 #pragma unroll
-      for (int kk = 0; kk < C / 4; kk += 4) {
-        const float4 a4 = load4(ttr + kk);
-        const int s = g4 * (C / 4) + kk;
-        uacc = mfma4(a4.x, Vs[(s + 0) * kUP + l16], uacc);
-        uacc = mfma4(a4.y, Vs[(s + 1) * kUP + l16], uacc);
-        uacc = mfma4(a4.z, Vs[(s + 2) * kUP + l16], uacc);
-        uacc = mfma4(a4.w, Vs[(s + 3) * kUP + l16], uacc);
-      }
-      const float* wr = u.w + trow * S + g4 * (S / 4);
-      const float* qr = qn + (int64_t)(t0 + trow) * kq_tok + g4 * (S / 4);
-      const float* mr = Ms + l16 * kMP + g4 * (S / 4);
-      const float gam = Gam[trow];
-#pragma unroll
-      for (int kk = 0; kk < S / 4; kk += 4) {
-        const float4 w4 = load4(wr + kk);
-        const float4 m4 = load4(mr + kk);
-        float4 q4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (tok_ok) q4 = load4(qr + kk);
-        uacc = mfma4(-w4.x, m4.x, uacc);
-        yacc = mfma4(gam * q4.x, m4.x, yacc);
-        uacc = mfma4(-w4.y, m4.y, uacc);
-        yacc = mfma4(gam * q4.y, m4.y, yacc);
-        uacc = mfma4(-w4.z, m4.z, uacc);
-        yacc = mfma4(gam * q4.z, m4.z, yacc);
-        uacc = mfma4(-w4.w, m4.w, uacc);
-        yacc = mfma4(gam * q4.w, m4.w, yacc);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int s0 = g4 * (C / 4) + 4 * j;
+      uacc = mfma4(f.tt[j].x, Vs[(s0 + 0) * kUP + l16], uacc);
+      uacc = mfma4(f.tt[j].y, Vs[(s0 + 1) * kUP + l16], uacc);
+      uacc = mfma4(f.tt[j].z, Vs[(s0 + 2) * kUP + l16], uacc);
+      uacc = mfma4(f.tt[j].w, Vs[(s0 + 3) * kUP + l16], uacc);
     }
+    const float gam = Gam[trow];
+    const float* mr = Ms + l16 * kMP + g4 * (S / 4);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float4 m4 = load4(mr + 4 * j);
+      uacc = mfma4(-f.w[j].x, m4.x, uacc);
+      yacc = mfma4(gam * f.q[j].x, m4.x, yacc);
+      uacc = mfma4(-f.w[j].y, m4.y, uacc);
+      yacc = mfma4(gam * f.q[j].y, m4.y, yacc);
+      uacc = mfma4(-f.w[j].z, m4.z, uacc);
+      yacc = mfma4(gam * f.q[j].z, m4.z, yacc);
+      uacc = mfma4(-f.w[j].w, m4.w, uacc);
+      yacc = mfma4(gam * f.q[j].w, m4.w, yacc);
+    }
+    fetch_a(nx, f);
 #pragma unroll
     for (int i = 0; i < 4; ++i) Us[(wv * 16 + g4 * 4 + i) * kUP + l16] = uacc[i];
     __syncthreads();
 
-    // Y += P U ; y out
-    {
-      const float* pr = u.p + trow * C + g4 * (C / 4);
+    // y += P U, and out
 #pragma unroll
-      for (int kk = 0; kk < C / 4; kk += 4) {
-        const float4 a4 = load4(pr + kk);
-        const int s = g4 * (C / 4) + kk;
-        yacc = mfma4(a4.x, Us[(s + 0) * kUP + l16], yacc);
-        yacc = mfma4(a4.y, Us[(s + 1) * kUP + l16], yacc);
-        yacc = mfma4(a4.z, Us[(s + 2) * kUP + l16], yacc);
-        yacc = mfma4(a4.w, Us[(s + 3) * kUP + l16], yacc);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int s0 = g4 * (C / 4) + 4 * j;
+      yacc = mfma4(f.p[j].x, Us[(s0 + 0) * kUP + l16], yacc);
+      yacc = mfma4(f.p[j].y, Us[(s0 + 1) * kUP + l16], yacc);
+      yacc = mfma4(f.p[j].z, Us[(s0 + 2) * kUP + l16], yacc);
+      yacc = mfma4(f.p[j].w, Us[(s0 + 3) * kUP + l16], yacc);
+    }
+    fetch_p(nx, f);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + wv * 16 + g4 * 4 + i;
-        if (t < n_tokens) yn[(int64_t)t * v_tok + l16] = scale * yacc[i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + wv * 16 + g4 * 4 + i;
+      if (t < n_tokens) yn[(int64_t)t * v_tok + l16] = scale * yacc[i];
     }
     // state update of this wave's column tiles: M = gamma_C M + U^T Kt
-    {
-      const float gam_c = Gam[C - 1];
+    const float gam_c = Gam[C - 1];
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const int col = (wv * 2 + c2) * 16 + l16;
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int col = (wv * 2 + c2) * 16 + l16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) macc[c2][i] *= gam_c;
+      for (int i = 0; i < 4; ++i) macc[c2][i] *= gam_c;
 #pragma unroll
-        for (int kk = 0; kk < C / 4; ++kk) {
-          const int s = g4 * (C / 4) + kk;
-          const float a = Us[s * kUP + l16];
-          float b = 0.0f;
-          if (t0 + s < n_tokens) b = kn[(int64_t)(t0 + s) * kq_tok + col] * Ktf[s];
-          macc[c2] = mfma4(a, b, macc[c2]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Ms[(g4 * 4 + i) * kMP + col] = macc[c2][i];
+      for (int kk = 0; kk < C / 4; ++kk) {
+        const int s0 = g4 * (C / 4) + kk;
+        macc[c2] = mfma4(Us[s0 * kUP + l16], Ks[s0 * kKSP + col] * Ktf[s0], macc[c2]);
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Ms[(g4 * 4 + i) * kMP + col] = macc[c2][i];
     }
     __syncthreads();
   }

@@ -41,6 +41,16 @@ inline unsigned grid_for(int64_t items, int per_block) {
   return (unsigned)((items + per_block - 1) / per_block);
 }
 
+// The dispatcher hands workgroup b to XCD b % 8. This maps a block id to a
+// logical block so that consecutive logical blocks share an XCD (and its L2),
+// when the grid divides evenly.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ unsigned xcd_group(unsigned bid, unsigned nblocks) {
+  if (nblocks % kXcds != 0) return bid;
+  return (bid % kXcds) * (nblocks / kXcds) + bid / kXcds;
+}
+
 // Internal launchers shared between translation units (no argument checks:
 // the calling entry point has validated everything).
 int launch_gated_rmsnorm_bf16z(const float* y, const float* w, const uint16_t* z, float* out,

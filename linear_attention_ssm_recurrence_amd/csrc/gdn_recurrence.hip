@@ -265,14 +265,6 @@ struct ScanCfg {
   static_assert(CT <= THREADS, "one staging thread per token");
 };
 
-constexpr int kXcds = 8;
-
-// Block id -> logical block, so that logical blocks b and b+1 share an XCD.
-__device__ __forceinline__ unsigned xcd_group(unsigned bid, unsigned nblocks) {
-  if (nblocks % kXcds != 0) return bid;
-  return (bid % kXcds) * (nblocks / kXcds) + bid / kXcds;
-}
-
 template <int S, bool SNAP>
 __global__ __launch_bounds__(ScanCfg<S>::THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void recurrence_scan_kernel(
