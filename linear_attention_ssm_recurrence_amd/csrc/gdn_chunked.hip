@@ -33,11 +33,15 @@
 //
 // MFMA v_mfma_f32_16x16x4f32 (checked on MI355X): lane l supplies
 // A[l%16][l/16] and B[l/16][l%16]; output element i of lane l is
-// D[4*(l/16) + i][l%16]. A dot product's k range is split as
-// k = (l/16)*KS + kk over the MFMA steps kk (KS = K/4), which makes the
-// operands of consecutive steps contiguous in memory: each lane reads them as
-// float4. Accumulation order therefore differs from the sequential scan;
-// results agree with it within the fp32 tolerance, not bit for bit.
+// D[4*(l/16) + i][l%16]. The scan splits a dot product's k range as
+// k = 16j + 4*(l/16) + c over the MFMA steps (j, c): a lane's operands for
+// four consecutive steps are contiguous (one float4), the four lane groups of
+// a row read 64 contiguous bytes, and LDS reads of a pitch-4 (mod 8) array
+// see only the unavoidable 2-way bank split. The workspace matrices are
+// stored in that lane order ("fragment order": 16 x 16 tiles of 256 floats,
+// float4 of lane l at 4l), so each operand load is one contiguous 1 KB.
+// Accumulation order differs from the sequential scan; results agree with it
+// within the fp32 tolerance, not bit for bit.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -57,10 +61,19 @@ __device__ __forceinline__ f32x4v mfma4(float a, float b, f32x4v c) {
 struct ChunkUnit {   // views into one unit of the workspace
   float* gam; // [C]      gamma_t = exp(Gc_t)
   float* ktf; // [C]      gamma_C / gamma_s
-  float* tt;  // [C][C]   X diag(beta)
-  float* p;   // [C][C]   (gamma_t/gamma_s) q_t.k_s, s <= t
-  float* w;   // [C][S]   X diag(beta gamma) K
+  float* tt;  // [C][C]   X diag(beta), fragment order
+  float* p;   // [C][C]   (gamma_t/gamma_s) q_t.k_s for s <= t, else 0; fragment order
+  float* w;   // [C][S]   -X diag(beta gamma) K, fragment order
 };
+
+// Offset of element (r, c) of a 16 x 16 tile in fragment order.
+__device__ __forceinline__ int frag_off(int r, int c) {
+  return (((c >> 2) & 3) * 16 + r) * 4 + (c & 3);
+}
+// Offset of element (t, s) of a matrix with nj 16-column tiles per tile row.
+__device__ __forceinline__ int frag_index(int t, int s, int nj) {
+  return ((t >> 4) * nj + (s >> 4)) * 256 + frag_off(t & 15, s & 15);
+}
 
 __device__ __forceinline__ ChunkUnit chunk_unit(float* ws, int64_t unit) {
   float* base = ws + unit * kChUnit;
@@ -139,13 +152,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
   // K K^T and Q K^T on the lower tiles (ti >= tj): 10 tiles each, 20 per
   // block, 5 per wave (tile id = wv + 4m: ids 0..9 are K K^T, 10..19 Q K^T)
   const int g4 = lane >> 4, l16 = lane & 15;
-  auto tile_of = [](int idx, int& ti, int& tj) {
+  auto tile_of = [](int idx, int& ti, int& tj) {   // idx % 10 -> (ti >= tj)
     const int tix = idx % 10;
-    ti = 0, tj = tix;
-    while (tj > ti) {
-      tj -= ti + 1;
-      ++ti;
-    }
+    ti = (tix >= 1) + (tix >= 3) + (tix >= 6);
+    tj = tix - ti * (ti + 1) / 2;
   };
   f32x4v acc5[5];
 #pragma unroll
@@ -180,14 +190,14 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
       if (idx < 10) {
         As[t * kAP + s] = (s < t) ? Bs[t] * r * acc5[m][i] : 0.0f;
       } else {
-        u.p[t * C + s] = (s <= t) ? r * acc5[m][i] : 0.0f;
+        u.p[frag_index(t, s, 4)] = (s <= t) ? r * acc5[m][i] : 0.0f;
       }
     }
   }
-  // upper tiles: A is not read there; P is stored as zero
-  for (int f = tid; f < C * C; f += 256) {
-    const int t = f / C, s = f % C;
-    if ((s >> 4) > (t >> 4)) u.p[f] = 0.0f;
+  // upper tiles: A is not read there; P is stored as zero (whole tiles)
+  for (int f = tid; f < 16 * 256; f += 256) {
+    const int tile = f >> 8, ti = tile >> 2, tj = tile & 3;
+    if (tj > ti) u.p[f] = 0.0f;
   }
   __syncthreads();
 
@@ -246,24 +256,30 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     }
     __syncthreads();
   }
-  // Tt = X diag(beta)
-  for (int f = tid; f < C * C; f += 256) {
-    const int t = f / C, s = f % C;
-    u.tt[f] = Xs[t * kAP + s] * Bs[s];
+  // Tt = X diag(beta), written in fragment order (one float4 per thread and step)
+  for (int f4 = tid; f4 < C * C / 4; f4 += 256) {
+    const int tile = f4 >> 6, ln = f4 & 63;
+    const int t = (tile >> 2) * 16 + (ln & 15), s0 = (tile & 3) * 16 + (ln >> 4) * 4;
+    const float* xr = Xs + t * kAP + s0;
+    store4(u.tt + 4 * f4, make_float4(xr[0] * Bs[s0], xr[1] * Bs[s0 + 1], xr[2] * Bs[s0 + 2],
+                                      xr[3] * Bs[s0 + 3]));
   }
-  // W = X diag(beta gamma) K: 4 x 8 output tiles of 16 x 16, 8 per wave
+  // -W = -X diag(beta gamma) K: 4 x 8 output tiles of 16 x 16, 8 per wave
   for (int tile = wv; tile < 32; tile += 4) {
     const int ti = tile >> 3, tc = tile & 7;
     f32x4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < C / 4; ++kk) {
-      const int s = g4 * (C / 4) + kk;
-      const float a = Xs[(ti * 16 + l16) * kAP + s] * BG[s];
-      const float b = Ks[s * kKP + tc * 16 + l16];
-      acc = mfma4(a, b, acc);
+    for (int j = 0; j < C / 16; ++j) {
+      const int s0 = 16 * j + 4 * g4;
+      const float4 x4 = load4(Xs + (ti * 16 + l16) * kAP + s0);
+      const float* kb = Ks + s0 * kKP + tc * 16 + l16;
+      acc = mfma4(x4.x * BG[s0], kb[0], acc);
+      acc = mfma4(x4.y * BG[s0 + 1], kb[kKP], acc);
+      acc = mfma4(x4.z * BG[s0 + 2], kb[2 * kKP], acc);
+      acc = mfma4(x4.w * BG[s0 + 3], kb[3 * kKP], acc);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) u.w[(ti * 16 + g4 * 4 + i) * S + tc * 16 + l16] = acc[i];
+    for (int i = 0; i < 4; ++i) u.w[frag_index(ti * 16 + g4 * 4 + i, tc * 16 + l16, 8)] = -acc[i];
   }
 }
 
@@ -274,11 +290,11 @@ constexpr int kMP = kChS + 4;   // LDS pitch of the state rows
 constexpr int kUP = kChR + 4;   // LDS pitch of U and V
 constexpr int kKSP = kChS + 4;  // LDS pitch of the chunk's K
 
-// What one chunk needs from memory, per lane: the A-operand rows of Tt and P
-// (16 floats each), W and q (32 each) for the lane's position row, and this
-// thread's share of K (8 float4) and V (1 float4) for LDS staging. Each group
-// is refilled with the next chunk's values right after its last use, so the
-// loads overlap the rest of the chunk.
+// What one chunk needs from memory, per lane: the A-operand fragments of Tt,
+// P (4 float4 each) and -W (8) from the workspace, the lane's q row pieces
+// (8), and this thread's share of K (8 float4) and V (1) for LDS staging.
+// Each group is refilled with the next chunk's values right after its last
+// use, so the loads overlap the rest of the chunk.
 struct ChunkRegs {
   float4 tt[4], p[4], w[8], q[8], kst[8], v;
   float gam, ktf;
@@ -291,11 +307,12 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
                        int n_k_heads, int n_v_heads, int n_chunks, float scale) {
   constexpr int S = kChS, C = kChC, R = kChR;
   __shared__ float Ms[R * kMP];
-  __shared__ float Us[C * kUP];
+  __shared__ float Us[C * kUP];   // U
+  __shared__ float Uk[C * kUP];   // diag(gamma_C / gamma) U, for the state update
   __shared__ float Vs[C * kUP];
   __shared__ float Ks[C * kKSP];
-  __shared__ float Gam[C];   // gamma_t
-  __shared__ float Ktf[C];   // gamma_C / gamma_s
+  __shared__ float Gam[C];        // gamma_t
+  __shared__ float Ktf[C];        // gamma_C / gamma_s
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
@@ -331,27 +348,26 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
       const int fi = (j * 256 + tid) * 4, t = fi / S, col = fi % S;
       f.kst[j] = load4(kn + (int64_t)tok_clamp(t0 + t) * kq_tok + col);
     }
-    const int t = tid >> 2;
-    f.v = load4(vn + (int64_t)tok_clamp(t0 + t) * v_tok + (tid & 3) * 4);
+    f.v = load4(vn + (int64_t)tok_clamp(t0 + (tid >> 2)) * v_tok + (tid & 3) * 4);
     const ChunkUnit u = unit_of(chunk);
     f.gam = (wv == 0) ? u.gam[lane] : 0.0f;
     f.ktf = (wv == 0) ? u.ktf[lane] : 0.0f;
   };
-  auto fetch_a = [&](int chunk, ChunkRegs& f) {    // Tt, W, q rows
+  auto fetch_a = [&](int chunk, ChunkRegs& f) {    // Tt, -W fragments, q rows
     const ChunkUnit u = unit_of(chunk);
-    const int t = chunk * C + trow;
+    const float* qr = qn + (int64_t)tok_clamp(chunk * C + trow) * kq_tok + 4 * g4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f.tt[j] = load4(u.tt + trow * C + g4 * (C / 4) + 4 * j);
+    for (int j = 0; j < 4; ++j) f.tt[j] = load4(u.tt + ((wv * 4 + j) * 64 + lane) * 4);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      f.w[j] = load4(u.w + trow * S + g4 * (S / 4) + 4 * j);
-      f.q[j] = load4(qn + (int64_t)tok_clamp(t) * kq_tok + g4 * (S / 4) + 4 * j);
+      f.w[j] = load4(u.w + ((wv * 8 + j) * 64 + lane) * 4);
+      f.q[j] = load4(qr + 16 * j);
     }
   };
-  auto fetch_p = [&](int chunk, ChunkRegs& f) {    // P rows
+  auto fetch_p = [&](int chunk, ChunkRegs& f) {    // P fragments
     const ChunkUnit u = unit_of(chunk);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f.p[j] = load4(u.p + trow * C + g4 * (C / 4) + 4 * j);
+    for (int j = 0; j < 4; ++j) f.p[j] = load4(u.p + ((wv * 4 + j) * 64 + lane) * 4);
   };
 
   // state rows: LDS copy (B operand of the M^T products) and this wave's two
@@ -374,7 +390,7 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
   for (int chunk = 0; chunk < n_chunks; ++chunk) {
     const int t0 = chunk * C;
     const int nx = chunk + 1 < n_chunks ? chunk + 1 : chunk;   // last chunk: harmless re-read
-    // stage K, V and the decay factors, then start the next chunk's K, V, Gc
+    // stage K, V and the decay factors, then start the next chunk's K, V, factors
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int fi = (j * 256 + tid) * 4;
@@ -388,43 +404,47 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
     fetch_kv(nx, f);
     __syncthreads();
 
-    // U rows 16wv..16wv+15 = Tt V - W M^T ; y part 1 = gamma Q M^T
+    // U rows 16wv..16wv+15 = Tt V + (-W) M^T ; y part 1 = Q M^T
     f32x4v uacc = {0.f, 0.f, 0.f, 0.f}, yacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int s0 = g4 * (C / 4) + 4 * j;
-      uacc = mfma4(f.tt[j].x, Vs[(s0 + 0) * kUP + l16], uacc);
-      uacc = mfma4(f.tt[j].y, Vs[(s0 + 1) * kUP + l16], uacc);
-      uacc = mfma4(f.tt[j].z, Vs[(s0 + 2) * kUP + l16], uacc);
-      uacc = mfma4(f.tt[j].w, Vs[(s0 + 3) * kUP + l16], uacc);
+      const float* vb = Vs + (16 * j + 4 * g4) * kUP + l16;
+      uacc = mfma4(f.tt[j].x, vb[0], uacc);
+      uacc = mfma4(f.tt[j].y, vb[kUP], uacc);
+      uacc = mfma4(f.tt[j].z, vb[2 * kUP], uacc);
+      uacc = mfma4(f.tt[j].w, vb[3 * kUP], uacc);
     }
-    const float gam = Gam[trow];
-    const float* mr = Ms + l16 * kMP + g4 * (S / 4);
+    const float* mr = Ms + l16 * kMP + 4 * g4;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float4 m4 = load4(mr + 4 * j);
-      uacc = mfma4(-f.w[j].x, m4.x, uacc);
-      yacc = mfma4(gam * f.q[j].x, m4.x, yacc);
-      uacc = mfma4(-f.w[j].y, m4.y, uacc);
-      yacc = mfma4(gam * f.q[j].y, m4.y, yacc);
-      uacc = mfma4(-f.w[j].z, m4.z, uacc);
-      yacc = mfma4(gam * f.q[j].z, m4.z, yacc);
-      uacc = mfma4(-f.w[j].w, m4.w, uacc);
-      yacc = mfma4(gam * f.q[j].w, m4.w, yacc);
+      const float4 m4 = load4(mr + 16 * j);
+      uacc = mfma4(f.w[j].x, m4.x, uacc);
+      yacc = mfma4(f.q[j].x, m4.x, yacc);
+      uacc = mfma4(f.w[j].y, m4.y, uacc);
+      yacc = mfma4(f.q[j].y, m4.y, yacc);
+      uacc = mfma4(f.w[j].z, m4.z, uacc);
+      yacc = mfma4(f.q[j].z, m4.z, yacc);
+      uacc = mfma4(f.w[j].w, m4.w, uacc);
+      yacc = mfma4(f.q[j].w, m4.w, yacc);
     }
     fetch_a(nx, f);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Us[(wv * 16 + g4 * 4 + i) * kUP + l16] = uacc[i];
+    for (int i = 0; i < 4; ++i) {
+      const int r = wv * 16 + g4 * 4 + i;   // position of output element i
+      Us[r * kUP + l16] = uacc[i];
+      Uk[r * kUP + l16] = uacc[i] * Ktf[r];
+      yacc[i] *= Gam[r];                    // diag(gamma) Q M^T
+    }
     __syncthreads();
 
     // y += P U, and out
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int s0 = g4 * (C / 4) + 4 * j;
-      yacc = mfma4(f.p[j].x, Us[(s0 + 0) * kUP + l16], yacc);
-      yacc = mfma4(f.p[j].y, Us[(s0 + 1) * kUP + l16], yacc);
-      yacc = mfma4(f.p[j].z, Us[(s0 + 2) * kUP + l16], yacc);
-      yacc = mfma4(f.p[j].w, Us[(s0 + 3) * kUP + l16], yacc);
+      const float* ub = Us + (16 * j + 4 * g4) * kUP + l16;
+      yacc = mfma4(f.p[j].x, ub[0], yacc);
+      yacc = mfma4(f.p[j].y, ub[kUP], yacc);
+      yacc = mfma4(f.p[j].z, ub[2 * kUP], yacc);
+      yacc = mfma4(f.p[j].w, ub[3 * kUP], yacc);
     }
     fetch_p(nx, f);
 #pragma unroll
@@ -432,7 +452,7 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
       const int t = t0 + wv * 16 + g4 * 4 + i;
       if (t < n_tokens) yn[(int64_t)t * v_tok + l16] = scale * yacc[i];
     }
-    // state update of this wave's column tiles: M = gamma_C M + U^T Kt
+    // state update of this wave's column tiles: M = gamma_C M + (diag(Ktf) U)^T K
     const float gam_c = Gam[C - 1];
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
@@ -440,9 +460,14 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
 #pragma unroll
       for (int i = 0; i < 4; ++i) macc[c2][i] *= gam_c;
 #pragma unroll
-      for (int kk = 0; kk < C / 4; ++kk) {
-        const int s0 = g4 * (C / 4) + kk;
-        macc[c2] = mfma4(Us[s0 * kUP + l16], Ks[s0 * kKSP + col] * Ktf[s0], macc[c2]);
+      for (int j = 0; j < 4; ++j) {
+        const int s0 = 16 * j + 4 * g4;
+        const float* ua = Uk + s0 * kUP + l16;
+        const float* kb = Ks + s0 * kKSP + col;
+        macc[c2] = mfma4(ua[0], kb[0], macc[c2]);
+        macc[c2] = mfma4(ua[kUP], kb[kKSP], macc[c2]);
+        macc[c2] = mfma4(ua[2 * kUP], kb[2 * kKSP], macc[c2]);
+        macc[c2] = mfma4(ua[3 * kUP], kb[3 * kKSP], macc[c2]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) Ms[(g4 * 4 + i) * kMP + col] = macc[c2][i];
