@@ -285,14 +285,17 @@ int gdn_prefill_bf16(const uint16_t *qkv, const uint16_t *z, const float *a, con
 /*
  * Workspace, in bytes, that gdn_recurrence_seq_chunked needs (0 for invalid
  * sizes or an unsupported state size): per (sequence, V-head, 64-position
- * chunk) 16448 floats.
+ * chunk) 8448 floats (per-position decay factors and beta, and two 64 x 64
+ * matrices).
  */
 size_t gdn_chunked_workspace_bytes(int n_seqs, int n_tokens, int n_v_heads, int state_size);
 
 /*
  * The scan of gdn_recurrence_seq_ex (no snapshots) in chunked form: the
  * positions are taken 64 at a time and the delta rule over a chunk is applied
- * as matrix products (WY-style blocking, fp32 MFMA). The pages name a chunked
+ * as matrix products (WY-style blocking, fp32 MFMA): a preparation kernel
+ * builds each chunk's (I + A)^-1 and masked Q K^T for all chunks in parallel,
+ * then a scan kernel carries the state through the chunks in order. The pages name a chunked
  * prefill and keep the sequential scan as its reference ([FM] "softplus"
  * comment and the sequential-scan section) without giving its algorithm.
  * Same arguments and layouts as gdn_recurrence_seq_ex, plus a caller-owned

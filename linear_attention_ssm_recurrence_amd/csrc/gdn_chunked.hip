@@ -10,25 +10,26 @@
 //   u_t = beta_t (v_t - gamma_t M0 k_t - sum_{s<t} (gamma_t/gamma_s)(k_s.k_t) u_s)
 // so with A[t][s] = beta_t (gamma_t/gamma_s)(k_t.k_s) (s < t) and
 // X = (I + A)^-1 (unit lower triangular):
-//   U  = Tt V - W M0^T,     Tt = X diag(beta),  W = X diag(beta gamma) K
+//   U  = X Z,   Z = diag(beta) V - diag(beta gamma) K M0^T
 //   Y  = scale (diag(gamma) Q M0^T + P U),  P[t][s] = (gamma_t/gamma_s)(q_t.k_s), s <= t
-//   M  = gamma_C M0 + U^T Kt,  Kt[s] = (gamma_C/gamma_s) k_s
+//   M  = gamma_C M0 + (diag(gamma_C/gamma) U)^T K
 // (U, V, Y are C x Dv with rows per position; Q, K are C x Dk.)
 //
 // Two kernels:
 //  chunk_prep_kernel  one block per (sequence, V-head, chunk), all chunks in
-//                     parallel: Gc, then K K^T and Q K^T (lower tiles, MFMA),
+//                     parallel: Gc (summed in fp64: under strong decay it
+//                     reaches thousands, where an fp32 difference Gc_t - Gc_s
+//                     would lose ~1e-4), K K^T and Q K^T (lower tiles, MFMA),
 //                     A and P, X blockwise (16 x 16 diagonal tiles by forward
-//                     substitution, the others by MFMA), W (MFMA). Writes
-//                     gamma, gamma_C/gamma, Tt, P, W to the workspace. Gc is
-//                     summed in fp64: with strong decay it reaches thousands,
-//                     where an fp32 difference Gc_t - Gc_s would lose ~1e-4.
+//                     substitution, the others by MFMA). Writes gamma,
+//                     gamma_C/gamma, beta, X and P to the workspace.
 //  chunk_scan_kernel  one block per (sequence, V-head, 16 state rows), the
 //                     chunks in order: the 16 rows stay on chip, and per chunk
-//                     each of the 4 waves does 128 MFMAs (U, Y, state update).
+//                     each of the 4 waves does 128 MFMAs (K M^T and Q M^T,
+//                     X Z, P U, the state update).
 // Positions past the end of the sequence in the last chunk are padded with
-// g = 0, beta = 0 and k = q = 0 in the preparation: their rows of A, Tt, W
-// and U and their columns of Tt are zero, so they leave the state unchanged,
+// g = 0, beta = 0 and k = q = 0 in the preparation: their rows of A, X Z and
+// U, and their entries of beta, are zero, so they leave the state unchanged,
 // and their y are not stored.
 //
 // MFMA v_mfma_f32_16x16x4f32 (checked on MI355X): lane l supplies
@@ -52,7 +53,8 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 constexpr int kChS = 128;     // state size
 constexpr int kChC = 64;      // chunk length
 constexpr int kChR = 16;      // state rows per scan block
-constexpr int kChUnit = 2 * kChC + 2 * kChC * kChC + kChC * kChS;  // floats per (seq, head, chunk)
+constexpr int kChHead = 4 * kChC;                                   // per-position factors
+constexpr int kChUnit = kChHead + 2 * kChC * kChC;                  // floats per (seq, head, chunk)
 
 __device__ __forceinline__ f32x4v mfma4(float a, float b, f32x4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -61,9 +63,9 @@ __device__ __forceinline__ f32x4v mfma4(float a, float b, f32x4v c) {
 struct ChunkUnit {   // views into one unit of the workspace
   float* gam; // [C]      gamma_t = exp(Gc_t)
   float* ktf; // [C]      gamma_C / gamma_s
-  float* tt;  // [C][C]   X diag(beta), fragment order
+  float* bet; // [C]      beta_t (0 past the end)
+  float* x;   // [C][C]   (I + A)^-1, fragment order
   float* p;   // [C][C]   (gamma_t/gamma_s) q_t.k_s for s <= t, else 0; fragment order
-  float* w;   // [C][S]   -X diag(beta gamma) K, fragment order
 };
 
 // Offset of element (r, c) of a 16 x 16 tile in fragment order.
@@ -77,8 +79,8 @@ __device__ __forceinline__ int frag_index(int t, int s, int nj) {
 
 __device__ __forceinline__ ChunkUnit chunk_unit(float* ws, int64_t unit) {
   float* base = ws + unit * kChUnit;
-  float* mats = base + 2 * kChC;
-  return {base, base + kChC, mats, mats + kChC * kChC, mats + 2 * kChC * kChC};
+  float* mats = base + kChHead;
+  return {base, base + kChC, base + 2 * kChC, mats, mats + kChC * kChC};
 }
 
 // ---------------------------------------------------------------------------
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
   __shared__ float Ks[C * kKP];
   __shared__ float Qs[QS];        // reused for A and X once Q K^T is done
   __shared__ double Gs[C];        // Gc in fp64: differences of large sums keep their precision
-  __shared__ float Bs[C], BG[C];
+  __shared__ float Bs[C];
   float* As = Qs;                 // [C][kAP]
   float* Xs = Qs + C * kAP;       // [C][kAP]
   float* Ts = Qs + 2 * C * kAP;   // [3][16][kTP]
@@ -143,10 +145,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
   }
   __syncthreads();
   if (tid < C) {
-    const float gam = expf((float)Gs[tid]);
-    u.gam[tid] = gam;
+    u.gam[tid] = expf((float)Gs[tid]);
     u.ktf[tid] = expf((float)(Gs[C - 1] - Gs[tid]));
-    BG[tid] = Bs[tid] * gam;             // beta_s gamma_s
+    u.bet[tid] = Bs[tid];
   }
 
   // K K^T and Q K^T on the lower tiles (ti >= tj): 10 tiles each, 20 per
@@ -256,30 +257,11 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     }
     __syncthreads();
   }
-  // Tt = X diag(beta), written in fragment order (one float4 per thread and step)
+  // X, written in fragment order (one float4 per thread and step)
   for (int f4 = tid; f4 < C * C / 4; f4 += 256) {
     const int tile = f4 >> 6, ln = f4 & 63;
     const int t = (tile >> 2) * 16 + (ln & 15), s0 = (tile & 3) * 16 + (ln >> 4) * 4;
-    const float* xr = Xs + t * kAP + s0;
-    store4(u.tt + 4 * f4, make_float4(xr[0] * Bs[s0], xr[1] * Bs[s0 + 1], xr[2] * Bs[s0 + 2],
-                                      xr[3] * Bs[s0 + 3]));
-  }
-  // -W = -X diag(beta gamma) K: 4 x 8 output tiles of 16 x 16, 8 per wave
-  for (int tile = wv; tile < 32; tile += 4) {
-    const int ti = tile >> 3, tc = tile & 7;
-    f32x4v acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < C / 16; ++j) {
-      const int s0 = 16 * j + 4 * g4;
-      const float4 x4 = load4(Xs + (ti * 16 + l16) * kAP + s0);
-      const float* kb = Ks + s0 * kKP + tc * 16 + l16;
-      acc = mfma4(x4.x * BG[s0], kb[0], acc);
-      acc = mfma4(x4.y * BG[s0 + 1], kb[kKP], acc);
-      acc = mfma4(x4.z * BG[s0 + 2], kb[2 * kKP], acc);
-      acc = mfma4(x4.w * BG[s0 + 3], kb[3 * kKP], acc);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) u.w[frag_index(ti * 16 + g4 * 4 + i, tc * 16 + l16, 8)] = -acc[i];
+    store4(u.x + 4 * f4, load4(Xs + t * kAP + s0));
   }
 }
 
@@ -290,14 +272,14 @@ constexpr int kMP = kChS + 4;   // LDS pitch of the state rows
 constexpr int kUP = kChR + 4;   // LDS pitch of U and V
 constexpr int kKSP = kChS + 4;  // LDS pitch of the chunk's K
 
-// What one chunk needs from memory, per lane: the A-operand fragments of Tt,
-// P (4 float4 each) and -W (8) from the workspace, the lane's q row pieces
-// (8), and this thread's share of K (8 float4) and V (1) for LDS staging.
-// Each group is refilled with the next chunk's values right after its last
-// use, so the loads overlap the rest of the chunk.
+// What one chunk needs from memory, per lane: the A-operand fragments of X
+// and P (4 float4 each) from the workspace, the lane's q row pieces (8), and
+// this thread's share of K (8 float4) and V (1) for LDS staging. Each group
+// is refilled with the next chunk's values right after its last use, so the
+// loads overlap the rest of the chunk.
 struct ChunkRegs {
-  float4 tt[4], p[4], w[8], q[8], kst[8], v;
-  float gam, ktf;
+  float4 x[4], p[4], q[8], kst[8], v;
+  float gam, ktf, bet;
 };
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -307,12 +289,14 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
                        int n_k_heads, int n_v_heads, int n_chunks, float scale) {
   constexpr int S = kChS, C = kChC, R = kChR;
   __shared__ float Ms[R * kMP];
+  __shared__ float Zs[C * kUP];   // Z = diag(beta) V - diag(beta gamma) K M^T
   __shared__ float Us[C * kUP];   // U
   __shared__ float Uk[C * kUP];   // diag(gamma_C / gamma) U, for the state update
   __shared__ float Vs[C * kUP];
   __shared__ float Ks[C * kKSP];
   __shared__ float Gam[C];        // gamma_t
   __shared__ float Ktf[C];        // gamma_C / gamma_s
+  __shared__ float Bet[C];        // beta_t
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
@@ -331,17 +315,16 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
   float* sp = state + head * (int64_t)S * S + (int64_t)row0 * S;
   const int trow = wv * 16 + l16;                     // this lane's A-operand row
   const int last_tok = n_tokens - 1;
-  // Positions past the end read the last valid row instead, unzeroed: the
-  // workspace operands are exactly zero there (beta = 0 makes those rows of
-  // Tt, W and U, and those columns of Tt, zero), so K and V rows meet only
-  // zeros, and q rows only reach y rows that are not stored. (Zeroing on
-  // load would make the compiler wait for each prefetch as it is issued.)
+  // Positions past the end read the last valid row instead, unzeroed: their
+  // beta and their columns of X are exactly zero, so K and V rows there meet
+  // only zeros, and q rows only reach y rows that are not stored. (Zeroing
+  // on load would make the compiler wait for each prefetch as it is issued.)
   auto tok_clamp = [&](int t) { return t < last_tok ? t : last_tok; };
 
   auto unit_of = [&](int chunk) {
     return chunk_unit(const_cast<float*>(ws), head * n_chunks + chunk);
   };
-  auto fetch_kv = [&](int chunk, ChunkRegs& f) {   // K, V, decay factors: staged through LDS
+  auto fetch_kv = [&](int chunk, ChunkRegs& f) {   // K, V, factors: staged through LDS
     const int t0 = chunk * C;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -352,17 +335,17 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
     const ChunkUnit u = unit_of(chunk);
     f.gam = (wv == 0) ? u.gam[lane] : 0.0f;
     f.ktf = (wv == 0) ? u.ktf[lane] : 0.0f;
+    f.bet = (wv == 0) ? u.bet[lane] : 0.0f;
   };
-  auto fetch_a = [&](int chunk, ChunkRegs& f) {    // Tt, -W fragments, q rows
-    const ChunkUnit u = unit_of(chunk);
+  auto fetch_q = [&](int chunk, ChunkRegs& f) {    // q row pieces
     const float* qr = qn + (int64_t)tok_clamp(chunk * C + trow) * kq_tok + 4 * g4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f.tt[j] = load4(u.tt + ((wv * 4 + j) * 64 + lane) * 4);
+    for (int j = 0; j < 8; ++j) f.q[j] = load4(qr + 16 * j);
+  };
+  auto fetch_x = [&](int chunk, ChunkRegs& f) {    // X fragments
+    const ChunkUnit u = unit_of(chunk);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      f.w[j] = load4(u.w + ((wv * 8 + j) * 64 + lane) * 4);
-      f.q[j] = load4(qr + 16 * j);
-    }
+    for (int j = 0; j < 4; ++j) f.x[j] = load4(u.x + ((wv * 4 + j) * 64 + lane) * 4);
   };
   auto fetch_p = [&](int chunk, ChunkRegs& f) {    // P fragments
     const ChunkUnit u = unit_of(chunk);
@@ -384,13 +367,14 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
 
   ChunkRegs f;
   fetch_kv(0, f);
-  fetch_a(0, f);
+  fetch_q(0, f);
+  fetch_x(0, f);
   fetch_p(0, f);
 
   for (int chunk = 0; chunk < n_chunks; ++chunk) {
     const int t0 = chunk * C;
     const int nx = chunk + 1 < n_chunks ? chunk + 1 : chunk;   // last chunk: harmless re-read
-    // stage K, V and the decay factors, then start the next chunk's K, V, factors
+    // stage K, V and the factors, then start the next chunk's K, V, factors
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int fi = (j * 256 + tid) * 4;
@@ -400,40 +384,54 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
     if (wv == 0) {
       Gam[lane] = f.gam;
       Ktf[lane] = f.ktf;
+      Bet[lane] = f.bet;
     }
     fetch_kv(nx, f);
     __syncthreads();
 
-    // U rows 16wv..16wv+15 = Tt V + (-W) M^T ; y part 1 = Q M^T
-    f32x4v uacc = {0.f, 0.f, 0.f, 0.f}, yacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float* vb = Vs + (16 * j + 4 * g4) * kUP + l16;
-      uacc = mfma4(f.tt[j].x, vb[0], uacc);
-      uacc = mfma4(f.tt[j].y, vb[kUP], uacc);
-      uacc = mfma4(f.tt[j].z, vb[2 * kUP], uacc);
-      uacc = mfma4(f.tt[j].w, vb[3 * kUP], uacc);
-    }
+    // rows 16wv..16wv+15 of K M^T and Q M^T (K from LDS, q from registers)
+    f32x4v zacc = {0.f, 0.f, 0.f, 0.f}, yacc = {0.f, 0.f, 0.f, 0.f};
     const float* mr = Ms + l16 * kMP + 4 * g4;
+    const float* kr = Ks + trow * kKSP + 4 * g4;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float4 m4 = load4(mr + 16 * j);
-      uacc = mfma4(f.w[j].x, m4.x, uacc);
+      const float4 k4 = load4(kr + 16 * j);
+      zacc = mfma4(k4.x, m4.x, zacc);
       yacc = mfma4(f.q[j].x, m4.x, yacc);
-      uacc = mfma4(f.w[j].y, m4.y, uacc);
+      zacc = mfma4(k4.y, m4.y, zacc);
       yacc = mfma4(f.q[j].y, m4.y, yacc);
-      uacc = mfma4(f.w[j].z, m4.z, uacc);
+      zacc = mfma4(k4.z, m4.z, zacc);
       yacc = mfma4(f.q[j].z, m4.z, yacc);
-      uacc = mfma4(f.w[j].w, m4.w, uacc);
+      zacc = mfma4(k4.w, m4.w, zacc);
       yacc = mfma4(f.q[j].w, m4.w, yacc);
     }
-    fetch_a(nx, f);
+    fetch_q(nx, f);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wv * 16 + g4 * 4 + i;   // position of output element i
+      const float b = Bet[r], gm = Gam[r];
+      Zs[r * kUP + l16] = b * Vs[r * kUP + l16] - (b * gm) * zacc[i];
+      yacc[i] *= gm;                         // diag(gamma) Q M^T
+    }
+    __syncthreads();
+
+    // U rows 16wv..16wv+15 = X Z
+    f32x4v uacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float* zb = Zs + (16 * j + 4 * g4) * kUP + l16;
+      uacc = mfma4(f.x[j].x, zb[0], uacc);
+      uacc = mfma4(f.x[j].y, zb[kUP], uacc);
+      uacc = mfma4(f.x[j].z, zb[2 * kUP], uacc);
+      uacc = mfma4(f.x[j].w, zb[3 * kUP], uacc);
+    }
+    fetch_x(nx, f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wv * 16 + g4 * 4 + i;
       Us[r * kUP + l16] = uacc[i];
       Uk[r * kUP + l16] = uacc[i] * Ktf[r];
-      yacc[i] *= Gam[r];                    // diag(gamma) Q M^T
     }
     __syncthreads();
 

@@ -184,7 +184,7 @@ def test_prefill_validation(lib):
 def test_chunked_validation(lib):
     f = lib.gdn_recurrence_seq_chunked
     need = lib.gdn_chunked_workspace_bytes(1, 100, 4, 128)
-    assert need == 1 * 4 * 2 * 16512 * 4
+    assert need == 1 * 4 * 2 * 8448 * 4
     assert lib.gdn_chunked_workspace_bytes(1, 100, 4, 64) == 0
 
     def call(state=FAKE, ws=FAKE, ws_bytes=need, T=100, HK=2, H=4, S=128):
