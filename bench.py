@@ -10,7 +10,8 @@ finds its state in the 256 MB Infinity Cache.
 
 The same line carries the other workloads of the hot path ("legs"):
   scan        1 sequence x 4096 tokens x 32 heads x S = 128: conv1d+SiLU over
-              the 4096 x 8192 activations, then the sequential scan; tokens/s
+              the 4096 x 8192 activations, then the chunked scan (the
+              sequential scan timed beside it); tokens/s
   block       64 sequences x 48 layers of the fused bf16 decode layer (conv,
               L2 norm + GQA repeat 16 -> 32, gate, sigmoid, recurrence, gated
               RMSNorm), one launch per layer; ms per 48-layer step
@@ -19,8 +20,9 @@ The same line carries the other workloads of the hot path ("legs"):
               recurrence
   decode_t4   the headline batch with the "T4" read-out (gdn_recurrence_ex)
   prefill     one bf16 layer over 1 sequence x 4096 positions through
-              gdn_prefill_bf16 (fused conv/norm/gate front end, scan with the
-              16 -> 32 repeat by index, gated norm); tokens/s
+              gdn_prefill_bf16_ex (fused conv/norm/gate front end, chunked scan
+              with the 16 -> 32 repeat by index, gated norm; the sequential
+              scan timed beside it); tokens/s
   spec        a speculative-decoding verify step: 64 sequences x 4 draft
               tokens, 16 -> 32 heads by index, S = 128, conv over C = 8192,
               with per-token state and conv snapshots
@@ -223,8 +225,12 @@ def run_scan(torch, gdn, inputs, steps, warmup):
 
     for _ in range(warmup):
         conv()
-        scan()
+        chunked()
     with Timer(torch) as t_all:
+        for _ in range(steps):
+            conv()
+            chunked()
+    with Timer(torch) as t_all_seq:
         for _ in range(steps):
             conv()
             scan()
@@ -234,8 +240,6 @@ def run_scan(torch, gdn, inputs, steps, warmup):
     with Timer(torch) as t_scan:
         for _ in range(steps):
             scan()
-    for _ in range(warmup):
-        chunked()
     with Timer(torch) as t_chunk:
         for _ in range(steps):
             chunked()
@@ -246,10 +250,11 @@ def run_scan(torch, gdn, inputs, steps, warmup):
     conv_bytes = 2 * N * T * C * 4 + C * w.conv_kernel * 4 + 2 * N * C * (w.conv_kernel - 1) * 4
     scan_bytes = (4 * N * T * H * S + 2 * N * T * H) * 4 + 2 * N * H * S * S * 4
     return {
-        "workload": "sequential scan: 1 sequence x 4096 tokens x 32 heads x S=128 fp32, "
+        "workload": "scan: 1 sequence x 4096 tokens x 32 heads x S=128 fp32, chunked form, "
                     "preceded by conv1d+SiLU over 4096 x 8192 (K=4)",
         "ms_per_step": ms,
         "tokens_per_s": N * T / (ms * 1e-3),
+        "sequential_ms_per_step": t_all_seq.wall_ms / steps,
         "scan_kernel_ms": scan_ms,
         "scan_tokens_per_s": N * T / (scan_ms * 1e-3),
         "scan_TFLOPs": flops / (scan_ms * 1e-3) / 1e12,
@@ -321,20 +326,25 @@ def run_prefill(torch, gdn, inputs, steps, warmup):
     scale = 1.0 / math.sqrt(S)
     torch.cuda.synchronize()
 
-    def step():
+    def step(scan):
         gdn.gdn_prefill_bf16(t["qkv"], t["z"], t["a"], t["b"], t["conv_w"], t["A_log"],
                              t["dt_bias"], t["norm_w"], t["conv_state"], t["state"], out, ws, HK,
-                             scale)
+                             scale, scan=scan)
 
-    for _ in range(warmup):
-        step()
-    with Timer(torch) as tm:
-        for _ in range(steps):
-            step()
-    ms = tm.wall_ms / steps
+    ms = {}
+    for scan in (gdn.GDN_SCAN_CHUNKED, gdn.GDN_SCAN_SEQUENTIAL):
+        for _ in range(warmup):
+            step(scan)
+        with Timer(torch) as tm:
+            for _ in range(steps):
+                step(scan)
+        ms[scan] = tm.wall_ms / steps
+    chunk_ms, seq_ms = ms[gdn.GDN_SCAN_CHUNKED], ms[gdn.GDN_SCAN_SEQUENTIAL]
     return {"workload": "bf16 prefill of one layer: 1 sequence x 4096 positions, 16 -> 32 heads, "
-                        "S=128, C=8192, K=4",
-            "ms_per_step": ms, "tokens_per_s": N * T / (ms * 1e-3)}
+                        "S=128, C=8192, K=4, chunked scan",
+            "ms_per_step": chunk_ms, "tokens_per_s": N * T / (chunk_ms * 1e-3),
+            "sequential_ms_per_step": seq_ms,
+            "sequential_tokens_per_s": N * T / (seq_ms * 1e-3)}
 
 
 def block_layer_bytes(N, H, HK, S, K) -> int:

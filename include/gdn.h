@@ -243,8 +243,9 @@ int gdn_decode_block_bf16(const uint16_t *qkv, const uint16_t *z, const float *a
                           void *stream);
 
 /*
- * Workspace, in bytes, that gdn_prefill_bf16 needs for these sizes (0 for
- * invalid sizes): normalised q and k per K-head, v, g, beta and y, fp32.
+ * Workspace, in bytes, that gdn_prefill_bf16 and gdn_prefill_bf16_ex (either
+ * scan) need for these sizes (0 for invalid sizes): normalised q and k per
+ * K-head, v, g, beta and y, fp32, and the chunked scan's workspace.
  */
 size_t gdn_prefill_workspace_bytes(int n_seqs, int n_tokens, int n_k_heads, int n_v_heads,
                                    int state_size);
@@ -310,6 +311,24 @@ int gdn_recurrence_seq_chunked(float *state, const float *q, const float *k, con
                                const float *g, const float *beta, float *y, void *workspace,
                                size_t workspace_bytes, int n_seqs, int n_tokens, int n_k_heads,
                                int n_v_heads, int state_size, float scale, void *stream);
+
+#define GDN_SCAN_SEQUENTIAL 0 /* the scan of gdn_recurrence_seq_ex */
+#define GDN_SCAN_CHUNKED 1    /* the scan of gdn_recurrence_seq_chunked */
+
+/*
+ * gdn_prefill_bf16 with a choice of scan for stage 2. GDN_SCAN_SEQUENTIAL is
+ * gdn_prefill_bf16 itself (equal to chained gdn_decode_block_bf16 calls bit
+ * for bit); GDN_SCAN_CHUNKED runs the chunked form of the same scan, which
+ * agrees with it within the fp32 tolerance. Same arguments, layouts and
+ * workspace as gdn_prefill_bf16.
+ * Errors: as gdn_prefill_bf16, and GDN_EUNSUPPORTED for an unknown scan.
+ */
+int gdn_prefill_bf16_ex(const uint16_t *qkv, const uint16_t *z, const float *a, const float *b,
+                        const float *conv_w, const float *A_log, const float *dt_bias,
+                        const float *norm_w, float *conv_state, float *state, float *out,
+                        void *workspace, size_t workspace_bytes, int n_seqs, int n_tokens,
+                        int n_k_heads, int n_v_heads, int state_size, int conv_kernel, float scale,
+                        float l2_eps, float eps, int scan, void *stream);
 
 #ifdef __cplusplus
 }

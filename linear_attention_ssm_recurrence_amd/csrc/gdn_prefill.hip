@@ -5,12 +5,13 @@
 // kernels, chained: conv1d + SiLU over the positions, L2 norm of q and k per
 // K-head, v passed through, decay gate and sigmoid per position, the
 // sequential scan (V-head h reading K-head h mod HK), then the gated RMSNorm.
-// Three launches:
+// Three stages:
 //   1. prefill_frontend_kernel: conv + L2 norm + gate + sigmoid, fused;
-//   2. the scan of gdn_recurrence_seq_ex on its outputs;
+//   2. the scan on its outputs: the sequential scan of gdn_recurrence_seq_ex,
+//      or the chunked one of gdn_recurrence_seq_chunked (GDN_SCAN_CHUNKED);
 //   3. the gated RMSNorm with the bf16 gate z.
-// The intermediates (normalised q and k per K-head, v, g, beta, y) live in a
-// caller-provided workspace.
+// The intermediates (normalised q and k per K-head, v, g, beta, y, and the
+// chunked scan's workspace) live in a caller-provided workspace.
 //
 // Front end. A wave owns one "head part" (the S = 128 channels of q or k of a
 // K-head, or of v of a V-head) of one sequence over TB = 32 positions: lanes
@@ -23,8 +24,9 @@
 // write the new one.
 //
 // Every value goes through the same device function and reduction order as in
-// the fused decode layer (gdn_block.hip), so a prefill over T positions equals
-// T calls of gdn_decode_block_bf16 bit for bit.
+// the fused decode layer (gdn_block.hip), so with the sequential scan a
+// prefill over T positions equals T calls of gdn_decode_block_bf16 bit for
+// bit; the chunked scan agrees with them within the fp32 tolerance.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -37,6 +39,8 @@ constexpr int kPrefillWaves = 4;             // head parts per block
 
 struct PrefillWorkspace {
   float *q, *k, *v, *g, *beta, *y;
+  void* chunk;          // workspace of the chunked scan
+  size_t chunk_bytes;
 };
 
 inline size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
@@ -57,6 +61,9 @@ inline size_t prefill_layout(int64_t N, int64_t T, int64_t HK, int64_t H, int64_
   take(N * T * H, &w->g);
   take(N * T * H, &w->beta);
   take(N * T * H * S, &w->y);
+  w->chunk_bytes = gdn_chunked_workspace_bytes((int)N, (int)T, (int)H, (int)S);
+  if (base) w->chunk = base + off;
+  off += round256(w->chunk_bytes);
   return off;
 }
 
@@ -218,13 +225,14 @@ extern "C" size_t gdn_prefill_workspace_bytes(int n_seqs, int n_tokens, int n_k_
   return prefill_layout(n_seqs, n_tokens, n_k_heads, n_v_heads, state_size, nullptr, nullptr);
 }
 
-extern "C" int gdn_prefill_bf16(const uint16_t* qkv, const uint16_t* z, const float* a,
-                                const float* b, const float* conv_w, const float* A_log,
-                                const float* dt_bias, const float* norm_w, float* conv_state,
-                                float* state, float* out, void* workspace, size_t workspace_bytes,
-                                int n_seqs, int n_tokens, int n_k_heads, int n_v_heads,
-                                int state_size, int conv_kernel, float scale, float l2_eps,
-                                float eps, void* stream) {
+extern "C" int gdn_prefill_bf16_ex(const uint16_t* qkv, const uint16_t* z, const float* a,
+                                   const float* b, const float* conv_w, const float* A_log,
+                                   const float* dt_bias, const float* norm_w, float* conv_state,
+                                   float* state, float* out, void* workspace,
+                                   size_t workspace_bytes, int n_seqs, int n_tokens,
+                                   int n_k_heads, int n_v_heads, int state_size, int conv_kernel,
+                                   float scale, float l2_eps, float eps, int scan, void* stream) {
+  if (scan != GDN_SCAN_SEQUENTIAL && scan != GDN_SCAN_CHUNKED) return GDN_EUNSUPPORTED;
   if (n_seqs < 0 || n_tokens < 0 || n_k_heads <= 0 || n_v_heads <= 0 || state_size <= 0 ||
       conv_kernel <= 0)
     return GDN_ESIZE;
@@ -255,8 +263,26 @@ extern "C" int gdn_prefill_bf16(const uint16_t* qkv, const uint16_t* z, const fl
     case 4: rc = launch_frontend<4>(qkv, a, b, conv_w, A_log, dt_bias, conv_state, ws, n_seqs, n_tokens, n_k_heads, n_v_heads, l2_eps, s); break;
   }
   if (rc != GDN_OK) return rc;
-  rc = gdn_recurrence_seq_ex(state, ws.q, ws.k, ws.v, ws.g, ws.beta, ws.y, nullptr, n_seqs,
-                             n_tokens, n_k_heads, n_v_heads, state_size, scale, stream);
+  if (scan == GDN_SCAN_CHUNKED)
+    rc = gdn_recurrence_seq_chunked(state, ws.q, ws.k, ws.v, ws.g, ws.beta, ws.y, ws.chunk,
+                                    ws.chunk_bytes, n_seqs, n_tokens, n_k_heads, n_v_heads,
+                                    state_size, scale, stream);
+  else
+    rc = gdn_recurrence_seq_ex(state, ws.q, ws.k, ws.v, ws.g, ws.beta, ws.y, nullptr, n_seqs,
+                               n_tokens, n_k_heads, n_v_heads, state_size, scale, stream);
   if (rc != GDN_OK) return rc;
   return launch_gated_rmsnorm_bf16z(ws.y, norm_w, z, out, rows, state_size, eps, s);
+}
+
+extern "C" int gdn_prefill_bf16(const uint16_t* qkv, const uint16_t* z, const float* a,
+                                const float* b, const float* conv_w, const float* A_log,
+                                const float* dt_bias, const float* norm_w, float* conv_state,
+                                float* state, float* out, void* workspace, size_t workspace_bytes,
+                                int n_seqs, int n_tokens, int n_k_heads, int n_v_heads,
+                                int state_size, int conv_kernel, float scale, float l2_eps,
+                                float eps, void* stream) {
+  return gdn_prefill_bf16_ex(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out,
+                             workspace, workspace_bytes, n_seqs, n_tokens, n_k_heads, n_v_heads,
+                             state_size, conv_kernel, scale, l2_eps, eps, GDN_SCAN_SEQUENTIAL,
+                             stream);
 }

@@ -25,6 +25,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "gdn.h")
 
 GDN_OK, GDN_ENULL, GDN_ESIZE, GDN_EUNSUPPORTED, GDN_EALIGN, GDN_ELAUNCH = range(6)
 GDN_RECUR_EXACT, GDN_RECUR_T4 = 0, 1
+GDN_SCAN_SEQUENTIAL, GDN_SCAN_CHUNKED = 0, 1
 
 
 class GdnError(RuntimeError):
@@ -60,6 +61,7 @@ def load_library():
         "gdn_gated_rmsnorm": [P, P, P, P, L, I, F, P],
         "gdn_decode_block_bf16": [P] * 11 + [I] * 5 + [F] * 3 + [P],
         "gdn_prefill_bf16": [P] * 12 + [ctypes.c_size_t] + [I] * 6 + [F] * 3 + [P],
+        "gdn_prefill_bf16_ex": [P] * 12 + [ctypes.c_size_t] + [I] * 6 + [F] * 3 + [I, P],
         "gdn_recurrence_seq_chunked": [P] * 8 + [ctypes.c_size_t] + [I] * 5 + [F, P],
     }
     for name, args in sig.items():
@@ -295,12 +297,13 @@ def gdn_prefill_workspace_bytes(n_seqs, n_tokens, n_k_heads, n_v_heads, state_si
 
 
 def gdn_prefill_bf16(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out,
-                     workspace, n_k_heads, scale, l2_eps=1e-6, eps=1e-6, stream=None):
+                     workspace, n_k_heads, scale, l2_eps=1e-6, eps=1e-6, stream=None, scan=None):
     """One layer over T positions. qkv [N][T][C] and z [N][T][H][S] hold bf16
     bit patterns; a, b [N][T][H]; conv_w [C][K]; A_log, dt_bias [H]; norm_w [S];
     conv_state [N][C][K-1] and state [N][H][S][S] updated in place;
     out [N][T][H][S]; workspace a uint8 device tensor of at least
-    gdn_prefill_workspace_bytes(...) bytes."""
+    gdn_prefill_workspace_bytes(...) bytes. scan=None calls gdn_prefill_bf16;
+    GDN_SCAN_SEQUENTIAL or GDN_SCAN_CHUNKED call gdn_prefill_bf16_ex."""
     N, T, H, S = z.shape
     C, K = conv_w.shape
     _shape(qkv, (N, T, C), "qkv")
@@ -314,12 +317,16 @@ def gdn_prefill_bf16(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, s
     _shape(out, (N, T, H, S), "out")
     if C != 2 * n_k_heads * S + H * S:
         raise ValueError(f"conv_dim {C} != 2*n_k_heads*S + n_v_heads*S")
-    _call("gdn_prefill_bf16", _ptr16(qkv, "qkv"), _ptr16(z, "z"), _ptr(a, F32, "a"),
-          _ptr(b, F32, "b"), _ptr(conv_w, F32, "conv_w"), _ptr(A_log, F32, "A_log"),
-          _ptr(dt_bias, F32, "dt_bias"), _ptr(norm_w, F32, "norm_w"),
-          _ptr(conv_state, F32, "conv_state"), _ptr(state, F32, "state"), _ptr(out, F32, "out"),
-          _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), N, T, n_k_heads, H, S, K,
-          float(scale), float(l2_eps), float(eps), _stream(z, stream))
+    args = (_ptr16(qkv, "qkv"), _ptr16(z, "z"), _ptr(a, F32, "a"),
+            _ptr(b, F32, "b"), _ptr(conv_w, F32, "conv_w"), _ptr(A_log, F32, "A_log"),
+            _ptr(dt_bias, F32, "dt_bias"), _ptr(norm_w, F32, "norm_w"),
+            _ptr(conv_state, F32, "conv_state"), _ptr(state, F32, "state"), _ptr(out, F32, "out"),
+            _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), N, T, n_k_heads, H, S, K,
+            float(scale), float(l2_eps), float(eps))
+    if scan is None:
+        _call("gdn_prefill_bf16", *args, _stream(z, stream))
+    else:
+        _call("gdn_prefill_bf16_ex", *args, int(scan), _stream(z, stream))
 
 
 def gdn_chunked_workspace_bytes(n_seqs, n_tokens, n_v_heads, state_size) -> int:

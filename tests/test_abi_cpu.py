@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_header_symbol(lib):
     names = gdn.header_symbols()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     out = os.popen(f"nm -D --defined-only {gdn.LIB_PATH}").read()
     exported = set(re.findall(r"\sT\s(gdn_\w+)", out))
     for name in names:
@@ -179,6 +179,23 @@ def test_prefill_validation(lib):
     assert call(K=1) == gdn.GDN_EUNSUPPORTED
     assert call(T=-1) == gdn.GDN_ESIZE
     assert call(first=NUL, ws=NUL, T=0) == gdn.GDN_OK
+
+
+def test_prefill_ex_validation(lib):
+    f = lib.gdn_prefill_bf16_ex
+    need = lib.gdn_prefill_workspace_bytes(1, 100, 2, 4, 128)
+    assert need >= lib.gdn_chunked_workspace_bytes(1, 100, 4, 128)
+
+    def call(first=FAKE, ws=FAKE, ws_bytes=need, T=100, S=128, scan=gdn.GDN_SCAN_CHUNKED):
+        return f(first, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, ws_bytes,
+                 1, T, 2, 4, S, 4, 0.1, 1e-6, 1e-6, scan, NUL)
+
+    assert call(scan=2) == gdn.GDN_EUNSUPPORTED
+    assert call(scan=-1) == gdn.GDN_EUNSUPPORTED
+    assert call(first=NUL) == gdn.GDN_ENULL
+    assert call(ws_bytes=need - 1) == gdn.GDN_ESIZE
+    assert call(S=64) == gdn.GDN_EUNSUPPORTED
+    assert call(first=NUL, ws=NUL, T=0, scan=gdn.GDN_SCAN_SEQUENTIAL) == gdn.GDN_OK
 
 
 def test_chunked_validation(lib):
