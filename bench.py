@@ -26,6 +26,13 @@ The same line carries the other workloads of the hot path ("legs"):
   spec        a speculative-decoding verify step: 64 sequences x 4 draft
               tokens, 16 -> 32 heads by index, S = 128, conv over C = 8192,
               with per-token state and conv snapshots
+  single      one sequence, one token (16 -> 32 heads, S = 128, C = 8192):
+              conv + recurrence + gated norm as three launches, and the fused
+              bf16 layer as one; microseconds per step of GPU time with warm
+              caches (a captured HIP graph replayed) and after a 1 GiB cache
+              flush, and per eager Python call (host-launch-bound)
+  machine     what this GPU achieves: a 1 GiB device copy (GB/s) and the
+              fp32 FMA-chain issue rate of gdn_probe_fma (TFLOP/s)
 and the roofline of the dominant kernel (the decode recurrence) measured with
 HIP events on the stream it runs on, and the CPU oracle timed on this host.
 
@@ -65,7 +72,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="decode,scan,block,decode_full,decode_t4,spec,prefill")
+    ap.add_argument("--legs",
+                    default="decode,scan,block,decode_full,decode_t4,spec,prefill,single,machine")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
@@ -347,6 +355,121 @@ def run_prefill(torch, gdn, inputs, steps, warmup):
             "sequential_tokens_per_s": N * T / (seq_ms * 1e-3)}
 
 
+def run_single(torch, gdn, inputs, steps, warmup):
+    """One sequence, one token: latency of the decode kernels."""
+    w = inputs.WORKLOADS[1]
+    d = inputs.draw(w)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    H, HK, S, C, K = w.n_v_heads, w.n_k_heads, w.state_size, w.conv_dim, w.conv_kernel
+    q = torch.empty((1, H, S), device="cuda")
+    k = torch.empty((1, H, S), device="cuda")
+    g = torch.empty((1, H), device="cuda")
+    beta = torch.empty((1, H), device="cuda")
+    gdn.gdn_l2norm_gqa(dev(d["q_raw"][:, 0]), q, w.l2_eps)
+    gdn.gdn_l2norm_gqa(dev(d["k_raw"][:, 0]), k, w.l2_eps)
+    gdn.gdn_decay_gate(dev(d["a"][:, 0]), dev(d["dt_bias"]), dev(d["A_log"]), g)
+    gdn.gdn_sigmoid(dev(d["b"][:, 0]), beta)
+    v, st, z = dev(d["v"][:, 0]), dev(d["state"]), dev(d["z"][:, 0])
+    x, cw, cs, nw = dev(d["x"][:, 0]), dev(d["conv_w"]), dev(d["conv_state"]), dev(d["norm_w"])
+    y = torch.empty((1, H, S), device="cuda")
+    out = torch.empty((1, H, S), device="cuda")
+    co = torch.empty((1, C), device="cuda")
+    # the fused bf16 layer on one sequence (layer 0 of the block workload's draws)
+    wb = inputs.WORKLOADS[4]
+    lb = inputs.draw_block_layer(0, wb, n_seqs=1)
+    bits = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
+    b_in = {key: (bits(val) if val.dtype == np.uint16 else dev(val)) for key, val in lb.items()}
+    b_out = torch.empty((1, H, S), device="cuda")
+    flush = torch.empty(256 * 1024 * 1024, device="cuda")    # 1 GiB > the 256 MB Infinity Cache
+    torch.cuda.synchronize()
+
+    def three():
+        gdn.gdn_conv1d_silu(x, cw, cs, co)
+        gdn.gdn_recurrence(st, q, k, v, g, beta, y, w.scale)
+        gdn.gdn_gated_rmsnorm(y, nw, z, out, w.eps)
+
+    def fused():
+        gdn.gdn_decode_block_bf16(b_in["qkv"], b_in["z"], b_in["a"], b_in["b"], b_in["conv_w"],
+                                  b_in["A_log"], b_in["dt_bias"], b_in["norm_w"],
+                                  b_in["conv_state"], b_in["state"], b_out, HK, wb.scale,
+                                  wb.l2_eps, wb.eps)
+
+    def eager_us(fn):
+        for _ in range(warmup):
+            fn()
+        with Timer(torch) as tm:
+            for _ in range(steps):
+                fn()
+        return tm.event_ms / steps * 1e3
+
+    def graph_us(fn, per_graph=20, replays=10):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(per_graph):
+                fn()
+        graph.replay()
+        with Timer(torch) as tm:
+            for _ in range(replays):
+                graph.replay()
+        return tm.event_ms / (replays * per_graph) * 1e3
+
+    def cold_us(fn, reps):
+        evs = []
+        for i in range(reps):
+            flush.fill_(float(i))
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in evs)[reps // 2] * 1e3   # median
+
+    reps = max(5, min(steps, 30))
+    alg = (2 * H * S * S * 4 + 4 * H * S * 4 + 2 * H * 4           # recurrence
+           + 2 * C * 4 + C * K * 4 + 2 * C * (K - 1) * 4           # conv
+           + 3 * H * S * 4 + S * 4)                                # gated norm
+    r = {"workload": "one sequence, one token: 16 -> 32 heads, S=128, C=8192, K=4",
+         "three_kernels_us_warm": graph_us(three), "three_kernels_us_flushed": cold_us(three, reps),
+         "three_kernels_us_eager": eager_us(three),
+         "fused_bf16_layer_us_warm": graph_us(fused), "fused_bf16_layer_us_flushed": cold_us(fused, reps),
+         "fused_bf16_layer_us_eager": eager_us(fused),
+         "three_kernels_algorithmic_bytes": alg}
+    r["three_kernels_GBps_flushed"] = alg / (r["three_kernels_us_flushed"] * 1e-6) / 1e9
+    return r
+
+
+def run_machine(torch, gdn, steps):
+    """What this GPU achieves: a plain device copy and the fp32 FMA issue rate."""
+    src = torch.ones(256 * 1024 * 1024, device="cuda")       # 1 GiB
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    reps = max(3, min(steps, 10))
+    with Timer(torch) as tc:
+        for _ in range(reps):
+            dst.copy_(src)
+    copy_gbps = 2 * src.numel() * 4 * reps / (tc.event_ms * 1e-3) / 1e9
+    del src, dst
+    blocks, iters = 256 * 8, 4096
+    out = torch.empty(blocks * 256, device="cuda")
+    gdn.gdn_probe_fma(out, iters)
+    with Timer(torch) as tf:
+        for _ in range(reps):
+            gdn.gdn_probe_fma(out, iters)
+    flops = blocks * 256 * iters * 32 * reps
+    return {"copy_1GiB_GBps": copy_gbps, "copy_frac_hbm_peak": copy_gbps / HBM_PEAK_GBS,
+            "fma_chain_TFLOPs": flops / (tf.event_ms * 1e-3) / 1e12,
+            "fma_chain_frac_fp32_peak": flops / (tf.event_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS}
+
+
 def block_layer_bytes(N, H, HK, S, K) -> int:
     C = 2 * HK * S + H * S
     return (2 * N * H * S * S * 4            # state read + write
@@ -450,19 +573,28 @@ def cpu_baseline(inputs, d, budget_s):
         lib.oracle_recurrence_seq(P(st), P(q), P(k), P(v), P(g), P(beta), P(y), n, 1, H, S,
                                   float(w.scale))
 
-    run()                                              # warm-up
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        run()
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 10000:
-            break
+    def timed(budget):
+        run()                                          # warm-up
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            run()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget or reps >= 10000:
+                return reps, el
+
     state_bytes = 2 * n * H * S * S * 4
-    return {"value": state_bytes * reps / el / 1e9, "unit": "GB/s", "cores": oracle.get_threads(),
+    reps, el = timed(budget_s)
+    oracle.set_threads(1)
+    reps1, el1 = timed(max(1.0, budget_s / 4))
+    oracle.set_threads(threads)
+    return {"value": state_bytes * reps / el / 1e9, "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{n} of the 256 sequences (all 32 V-heads, S=128): {reps} decode steps "
-                      f"in {el:.1f} s; state bytes read+written per second"}
+                      f"in {el:.1f} s; state bytes read+written per second",
+            "single_thread_value": state_bytes * reps1 / el1 / 1e9,
+            "single_thread_sample": f"the same {n} sequences on 1 thread: {reps1} decode steps "
+                                    f"in {el1:.1f} s"}
 
 
 def main():
@@ -513,6 +645,14 @@ def main():
     if "block" in legs:
         log("leg block: 64 seqs x 48 layers")
         out_legs["block"] = run_block(torch, gdn, inputs, K, W)
+        torch.cuda.empty_cache()
+    if "single" in legs:
+        log("leg single: one sequence, one token")
+        out_legs["single"] = run_single(torch, gdn, inputs, K, W)
+        torch.cuda.empty_cache()
+    if "machine" in legs:
+        log("leg machine: device copy and FMA-chain rate")
+        out_legs["machine"] = run_machine(torch, gdn, K)
         torch.cuda.empty_cache()
 
     if args.calibrate_copy:

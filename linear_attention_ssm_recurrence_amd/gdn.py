@@ -14,6 +14,7 @@ fallback path.
 from __future__ import annotations
 
 import ctypes
+import glob
 import os
 import re
 
@@ -63,6 +64,7 @@ def load_library():
         "gdn_prefill_bf16": [P] * 12 + [ctypes.c_size_t] + [I] * 6 + [F] * 3 + [P],
         "gdn_prefill_bf16_ex": [P] * 12 + [ctypes.c_size_t] + [I] * 6 + [F] * 3 + [I, P],
         "gdn_recurrence_seq_chunked": [P] * 8 + [ctypes.c_size_t] + [I] * 5 + [F, P],
+        "gdn_probe_fma": [P, I, I, F, F, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -80,9 +82,12 @@ def load_library():
 
 
 def header_symbols() -> list[str]:
-    """Names of the entry points declared in include/gdn.h."""
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int|size_t)\s*(gdn_\w+)\s*\(", text, re.M)))
+    """Names of the entry points declared in the headers under include/."""
+    names = set()
+    for path in sorted(glob.glob(os.path.join(os.path.dirname(HEADER), "*.h"))):
+        text = open(path).read()
+        names |= set(re.findall(r"^\s*(?:const\s+char\s*\*|int|size_t)\s*(gdn_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def strerror(code: int) -> str:
@@ -349,3 +354,14 @@ def gdn_recurrence_seq_chunked(state, q, k, v, g, beta, y, scale, workspace, str
           _ptr(k, F32, "k"), _ptr(v, F32, "v"), _ptr(g, F32, "g"), _ptr(beta, F32, "beta"),
           _ptr(y, F32, "y"), _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
           N, T, HK, H, S, float(scale), _stream(v, stream))
+
+
+def gdn_probe_fma(out, iters, a=0.999, b=1e-3, stream=None):
+    """Measurement probe (not a step of the method): out is a float32 device
+    tensor of n_blocks * 256 elements; runs n_blocks * 256 * iters * 32 flop
+    of dependent fp32 FMA chains."""
+    n = out.numel()
+    if n % 256 != 0:
+        raise ValueError("out must hold n_blocks * 256 floats")
+    _call("gdn_probe_fma", _ptr(out, F32, "out"), n // 256, int(iters), float(a), float(b),
+          _stream(out, stream))

@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_header_symbol(lib):
     names = gdn.header_symbols()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     out = os.popen(f"nm -D --defined-only {gdn.LIB_PATH}").read()
     exported = set(re.findall(r"\sT\s(gdn_\w+)", out))
     for name in names:
@@ -179,6 +179,14 @@ def test_prefill_validation(lib):
     assert call(K=1) == gdn.GDN_EUNSUPPORTED
     assert call(T=-1) == gdn.GDN_ESIZE
     assert call(first=NUL, ws=NUL, T=0) == gdn.GDN_OK
+
+
+def test_probe_validation(lib):
+    f = lib.gdn_probe_fma
+    assert f(FAKE, 0, 10, 1.0, 0.0, NUL) == gdn.GDN_ESIZE
+    assert f(FAKE, 4, 0, 1.0, 0.0, NUL) == gdn.GDN_ESIZE
+    assert f(FAKE, (1 << 20) + 1, 10, 1.0, 0.0, NUL) == gdn.GDN_ESIZE
+    assert f(NUL, 4, 10, 1.0, 0.0, NUL) == gdn.GDN_ENULL
 
 
 def test_prefill_ex_validation(lib):
