@@ -13,8 +13,11 @@
 // it every V-head vh = kh + r*HK (r < GQ = H/HK). The conv channels those
 // heads read (q and k of kh, v of each vh) are read by no other workgroup, so
 // each channel's history is rolled exactly once. The workgroup:
-//   0. issues the loads of all its state rows (GQ*S rows, 64 KiB per V-head)
-//      so that HBM latency overlaps phases 1-2;
+//   0. issues the small loads of phases 1-2 (conv inputs, gate inputs), then
+//      the loads of all its state rows (GQ*S rows, 64 KiB per V-head), so
+//      that the state's HBM transfer overlaps phases 1-2 (the hardware
+//      counts outstanding loads in issue order: loads issued after the state
+//      would have to wait for all of it);
 //   1. convolves its (2 + GQ)*S channels into LDS and rolls their history;
 //   2. L2-normalises q and k in LDS (waves 0 and 1); wave 2 computes beta and
 //      exp(g) of the GQ V-heads;
@@ -60,7 +63,39 @@ __global__ __launch_bounds__(64 * kBlockWaves) void decode_block_kernel(
   const int kh = blockIdx.x % n_k_heads;
   const int64_t n = blockIdx.x / n_k_heads;
 
-  // 0. state rows of this wave: combined row R = wv*RW + ... over the GQ heads
+  // 0a. inputs of the conv (channels ch = tid + ci * threads) and of the gate
+  constexpr int TPB = 64 * kBlockWaves;
+  constexpr int CPT = (NCH + TPB - 1) / TPB;      // conv channels per thread
+  float wc[CPT][K], hist[CPT][K - 1], xv[CPT];
+  float* csp[CPT];
+#pragma unroll
+  for (int ci = 0; ci < CPT; ++ci) {
+    const int ch = tid + ci * TPB;
+    if (ch < NCH) {
+      const int seg = ch / S, i = ch % S;
+      int64_t c;
+      if (seg == 0) c = (int64_t)kh * S + i;
+      else if (seg == 1) c = key_dim + (int64_t)kh * S + i;
+      else c = 2 * (int64_t)key_dim + (int64_t)(kh + (seg - 2) * n_k_heads) * S + i;
+#pragma unroll
+      for (int u = 0; u < K; ++u) wc[ci][u] = conv_w[c * K + u];
+      csp[ci] = conv_state + (n * C + c) * (K - 1);
+#pragma unroll
+      for (int u = 0; u < K - 1; ++u) hist[ci][u] = csp[ci][u];
+      xv[ci] = bf16_to_float(qkv[n * C + c]);
+    }
+  }
+  const bool gate_lane = (wv == 2 && lane < GQ);
+  float ga = 0.0f, gdt = 0.0f, gal = 0.0f, gb = 0.0f;
+  if (gate_lane) {
+    const int h = kh + lane * n_k_heads;
+    ga = a[n * n_v_heads + h];
+    gdt = dt_bias[h];
+    gal = A_log[h];
+    gb = b[n * n_v_heads + h];
+  }
+
+  // 0b. state rows of this wave: combined row R = wv*RW + ... over the GQ heads
   const int r_head = (wv * RW) / S;                 // which of the GQ V-heads
   const int vh = kh + r_head * n_k_heads;
   const int p = lane % L;
@@ -74,23 +109,15 @@ __global__ __launch_bounds__(64 * kBlockWaves) void decode_block_kernel(
       raw[it][m] = load4_stream(sp + (int64_t)(row0 + it * G) * S + 4 * (p + L * m));
 
   // 1. conv of the workgroup's channels
-  for (int ch = tid; ch < NCH; ch += 64 * kBlockWaves) {
-    const int seg = ch / S, i = ch % S;
-    int64_t c;
-    if (seg == 0) c = (int64_t)kh * S + i;
-    else if (seg == 1) c = key_dim + (int64_t)kh * S + i;
-    else c = 2 * (int64_t)key_dim + (int64_t)(kh + (seg - 2) * n_k_heads) * S + i;
-    float wc[K], hist[K - 1];
 #pragma unroll
-    for (int u = 0; u < K; ++u) wc[u] = conv_w[c * K + u];
-    float* cs = conv_state + (n * C + c) * (K - 1);
+  for (int ci = 0; ci < CPT; ++ci) {
+    const int ch = tid + ci * TPB;
+    if (ch < NCH) {
+      co[ch] = conv_point<K>(xv[ci], hist[ci], wc[ci]);
 #pragma unroll
-    for (int u = 0; u < K - 1; ++u) hist[u] = cs[u];
-    const float xv = bf16_to_float(qkv[n * C + c]);
-    co[ch] = conv_point<K>(xv, hist, wc);
-#pragma unroll
-    for (int u = 0; u + 1 < K - 1; ++u) cs[u] = hist[u + 1];
-    cs[K - 2] = xv;
+      for (int u = 0; u + 1 < K - 1; ++u) csp[ci][u] = hist[ci][u + 1];
+      csp[ci][K - 2] = xv[ci];
+    }
   }
   __syncthreads();
 
@@ -108,11 +135,10 @@ __global__ __launch_bounds__(64 * kBlockWaves) void decode_block_kernel(
       v.w = v.w * inv;
       store4(x + 4 * m, v);
     }
-  } else if (wv == 2 && lane < GQ) {
-    const int h = kh + lane * n_k_heads;
-    const float gv = decay_gate(a[n * n_v_heads + h], dt_bias[h], A_log[h]);
+  } else if (gate_lane) {
+    const float gv = decay_gate(ga, gdt, gal);
     gate_d[lane] = expf(gv);
-    gate_b[lane] = sigmoid(b[n * n_v_heads + h]);
+    gate_b[lane] = sigmoid(gb);
   }
   __syncthreads();
 
