@@ -100,7 +100,64 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(const float* __restr
     store4(orow + 4 * m, o);
   }
 }
+
+// The same norm for head_dim = 128, the workloads' size: a half-wave per row
+// (one float4 per lane), two rows per wave at a time and kNormIters pairs per
+// wave, with every load issued before any arithmetic. The sum of squares is
+// the per-lane FMA chain of row_sumsq followed by the first five butterfly
+// steps of group_sum<64>; in row_sumsq the other 32 lanes contribute exact
+// zeros to the sixth step, so the result is the same bit for bit.
+constexpr int kNormIters = 2;
+
+template <typename ZT>
+__global__ __launch_bounds__(256) void gated_rmsnorm_d128_kernel(
+    const float* __restrict__ y, const float* __restrict__ w, const ZT* __restrict__ z,
+    float* __restrict__ out, int64_t n_rows, float eps) {
+  constexpr int D = 128;
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  float4 yv[kNormIters], zv[kNormIters];
+  int64_t rows[kNormIters];
+#pragma unroll
+  for (int it = 0; it < kNormIters; ++it) {
+    rows[it] = (wave * kNormIters + it) * 2 + half;
+    const int64_t r = rows[it] < n_rows ? rows[it] : n_rows - 1;   // rows past the end: not stored
+    yv[it] = load4_stream(y + r * D + 4 * l32);
+    zv[it] = load_z4(z + r * D + 4 * l32);
+  }
+  const float4 wv = load4(w + 4 * l32);
+#pragma unroll
+  for (int it = 0; it < kNormIters; ++it) {
+    float ss = 0.0f;
+    ss = __builtin_fmaf(yv[it].x, yv[it].x, ss);
+    ss = __builtin_fmaf(yv[it].y, yv[it].y, ss);
+    ss = __builtin_fmaf(yv[it].z, yv[it].z, ss);
+    ss = __builtin_fmaf(yv[it].w, yv[it].w, ss);
+    ss = group_sum<32>(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+    float4 o;
+    o.x = yv[it].x * inv * wv.x * silu(zv[it].x);
+    o.y = yv[it].y * inv * wv.y * silu(zv[it].y);
+    o.z = yv[it].z * inv * wv.z * silu(zv[it].z);
+    o.w = yv[it].w * inv * wv.w * silu(zv[it].w);
+    if (rows[it] < n_rows) store4(out + rows[it] * D + 4 * l32, o);
+  }
+}
 #pragma clang fp contract(fast)
+
+template <typename ZT>
+int launch_gated_rmsnorm(const float* y, const float* w, const ZT* z, float* out, int64_t n_rows,
+                         int head_dim, float eps, hipStream_t s) {
+  if (head_dim == 128) {
+    const int64_t rows_per_block = 4 * 2 * kNormIters;
+    hipLaunchKernelGGL(gated_rmsnorm_d128_kernel<ZT>, dim3(grid_for(n_rows, rows_per_block)),
+                       dim3(256), 0, s, y, w, z, out, n_rows, eps);
+  } else {
+    hipLaunchKernelGGL(gated_rmsnorm_kernel<ZT>, dim3(grid_for(n_rows, 4)), dim3(256), 0, s, y, w,
+                       z, out, n_rows, head_dim, eps);
+  }
+  return launch_status();
+}
 
 }  // namespace gdn
 
@@ -153,16 +210,12 @@ extern "C" int gdn_gated_rmsnorm(const float* y, const float* w, const float* z,
   if (!y || !w || !z || !out) return GDN_ENULL;
   if (n_rows / 4 >= (int64_t(1) << 31)) return GDN_ESIZE;
   if (!aligned16(y) || !aligned16(w) || !aligned16(z) || !aligned16(out)) return GDN_EALIGN;
-  hipLaunchKernelGGL(gated_rmsnorm_kernel<float>, dim3(grid_for(n_rows, 4)), dim3(256), 0,
-                     as_stream(stream), y, w, z, out, n_rows, head_dim, eps);
-  return launch_status();
+  return launch_gated_rmsnorm<float>(y, w, z, out, n_rows, head_dim, eps, as_stream(stream));
 }
 
 namespace gdn {
 int launch_gated_rmsnorm_bf16z(const float* y, const float* w, const uint16_t* z, float* out,
                                int64_t n_rows, int head_dim, float eps, hipStream_t s) {
-  hipLaunchKernelGGL(gated_rmsnorm_kernel<uint16_t>, dim3(grid_for(n_rows, 4)), dim3(256), 0, s,
-                     y, w, z, out, n_rows, head_dim, eps);
-  return launch_status();
+  return launch_gated_rmsnorm<uint16_t>(y, w, z, out, n_rows, head_dim, eps, s);
 }
 }  // namespace gdn

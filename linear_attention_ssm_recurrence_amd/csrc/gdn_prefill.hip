@@ -150,12 +150,36 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_frontend_kernel(
     }
   }
 
+  // every input of the half-wave's positions, loaded before any arithmetic
+  // (positions past the end read the last one and are zeroed at use)
+  uint2 xbits[TH];
+#pragma unroll
+  for (int s = 0; s < TH; ++s) {
+    const int t = tb + s < n_tokens ? tb + s : n_tokens - 1;
+    xbits[s] = *reinterpret_cast<const uint2*>(xn + (int64_t)t * C + c);
+  }
+  // the decay gate and beta inputs of the wave's positions (v parts)
+  const bool gate_lane = (kind == 2 && lane < TB && t0 + lane < n_tokens);
+  const int64_t gidx = (n * (int64_t)n_tokens + (gate_lane ? t0 + lane : 0)) * n_v_heads + head;
+  float ga = 0.0f, gb = 0.0f, gdt = 0.0f, gal = 0.0f;
+  if (gate_lane) {
+    ga = a[gidx];
+    gb = b[gidx];
+    gdt = dt_bias[head];
+    gal = A_log[head];
+  }
+
   const int64_t HKS = (int64_t)n_k_heads * S, HS = (int64_t)n_v_heads * S;
+#pragma unroll
   for (int s = 0; s < TH; ++s) {  // the same trip count in every lane: reductions stay whole
     const int t = tb + s;
     const bool valid = t < n_tokens;
-    float xv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (valid) load_bf16x4(xn + (int64_t)t * C + c, xv);
+    float xv[4];
+    xv[0] = bf16_to_float((uint16_t)(xbits[s].x & 0xFFFFu));
+    xv[1] = bf16_to_float((uint16_t)(xbits[s].x >> 16));
+    xv[2] = bf16_to_float((uint16_t)(xbits[s].y & 0xFFFFu));
+    xv[3] = bf16_to_float((uint16_t)(xbits[s].y >> 16));
+    if (!valid) xv[0] = xv[1] = xv[2] = xv[3] = 0.0f;
     float o[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -190,13 +214,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_frontend_kernel(
       for (int u = 0; u < K - 1; ++u) cs[j * (K - 1) + u] = fin[j][u];
   }
   // decay gate and beta of the wave's positions, by the v parts
-  if (kind == 2 && lane < TB) {
-    const int t = t0 + lane;
-    if (t < n_tokens) {
-      const int64_t idx = (n * (int64_t)n_tokens + t) * n_v_heads + head;
-      go[idx] = decay_gate(a[idx], dt_bias[head], A_log[head]);
-      bo[idx] = sigmoid(b[idx]);
-    }
+  if (gate_lane) {
+    go[gidx] = decay_gate(ga, gdt, gal);
+    bo[gidx] = sigmoid(gb);
   }
 }
 
