@@ -292,11 +292,15 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
   __shared__ float Zs[C * kUP];   // Z = diag(beta) V - diag(beta gamma) K M^T
   __shared__ float Us[C * kUP];   // U
   __shared__ float Uk[C * kUP];   // diag(gamma_C / gamma) U, for the state update
-  __shared__ float Vs[C * kUP];
-  __shared__ float Ks[C * kKSP];
-  __shared__ float Gam[C];        // gamma_t
-  __shared__ float Ktf[C];        // gamma_C / gamma_s
-  __shared__ float Bet[C];        // beta_t
+  __shared__ float Ys[C * kUP];   // y of the chunk, stored after the chunk's last barrier
+  // K, V and the factors of a chunk, double-buffered: chunk c + 1's copy is
+  // written during chunk c, so a chunk needs three barriers (after Z, after
+  // U, at the end), not four
+  __shared__ float Vs[2][C * kUP];
+  __shared__ float Ks[2][C * kKSP];
+  __shared__ float Gam[2][C];     // gamma_t
+  __shared__ float Ktf[2][C];     // gamma_C / gamma_s
+  __shared__ float Bet[2][C];     // beta_t
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
@@ -365,34 +369,48 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
 #pragma unroll
     for (int i = 0; i < 4; ++i) macc[c2][i] = Ms[(g4 * 4 + i) * kMP + (wv * 2 + c2) * 16 + l16];
 
+  // K, V and the factors of a chunk from registers into LDS buffer b
+  auto stage = [&](int b, const ChunkRegs& f) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int fi = (j * 256 + tid) * 4;
+      store4(Ks[b] + (fi / S) * kKSP + fi % S, f.kst[j]);
+    }
+    store4(Vs[b] + (tid >> 2) * kUP + (tid & 3) * 4, f.v);
+    if (wv == 0) {
+      Gam[b][lane] = f.gam;
+      Ktf[b][lane] = f.ktf;
+      Bet[b][lane] = f.bet;
+    }
+  };
+  // y rows of chunk c from LDS to memory, a float4 per thread: each wave
+  // writes 16 positions x 64 contiguous bytes in one instruction (a store of
+  // the MFMA output layout directly would be 16 dword stores per chunk)
+  auto flush_y = [&](int chunk) {
+    const int r = tid >> 2, c4 = (tid & 3) * 4;
+    const int t = chunk * C + r;
+    if (t < n_tokens) store4(yn + (int64_t)t * v_tok + c4, load4(Ys + r * kUP + c4));
+  };
+
   ChunkRegs f;
   fetch_kv(0, f);
   fetch_q(0, f);
   fetch_x(0, f);
   fetch_p(0, f);
+  stage(0, f);
+  fetch_kv(n_chunks > 1 ? 1 : 0, f);
+  __syncthreads();
 
   for (int chunk = 0; chunk < n_chunks; ++chunk) {
-    const int t0 = chunk * C;
+    const int b = chunk & 1;
     const int nx = chunk + 1 < n_chunks ? chunk + 1 : chunk;   // last chunk: harmless re-read
-    // stage K, V and the factors, then start the next chunk's K, V, factors
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int fi = (j * 256 + tid) * 4;
-      store4(Ks + (fi / S) * kKSP + fi % S, f.kst[j]);
-    }
-    store4(Vs + (tid >> 2) * kUP + (tid & 3) * 4, f.v);
-    if (wv == 0) {
-      Gam[lane] = f.gam;
-      Ktf[lane] = f.ktf;
-      Bet[lane] = f.bet;
-    }
-    fetch_kv(nx, f);
-    __syncthreads();
+    const int nx2 = chunk + 2 < n_chunks ? chunk + 2 : n_chunks - 1;
+    if (chunk > 0) flush_y(chunk - 1);
 
     // rows 16wv..16wv+15 of K M^T and Q M^T (K from LDS, q from registers)
     f32x4v zacc = {0.f, 0.f, 0.f, 0.f}, yacc = {0.f, 0.f, 0.f, 0.f};
     const float* mr = Ms + l16 * kMP + 4 * g4;
-    const float* kr = Ks + trow * kKSP + 4 * g4;
+    const float* kr = Ks[b] + trow * kKSP + 4 * g4;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float4 m4 = load4(mr + 16 * j);
@@ -410,68 +428,87 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wv * 16 + g4 * 4 + i;   // position of output element i
-      const float b = Bet[r], gm = Gam[r];
-      Zs[r * kUP + l16] = b * Vs[r * kUP + l16] - (b * gm) * zacc[i];
+      const float bt = Bet[b][r], gm = Gam[b][r];
+      Zs[r * kUP + l16] = bt * Vs[b][r * kUP + l16] - (bt * gm) * zacc[i];
       yacc[i] *= gm;                         // diag(gamma) Q M^T
     }
     __syncthreads();
 
-    // U rows 16wv..16wv+15 = X Z
-    f32x4v uacc = {0.f, 0.f, 0.f, 0.f};
+    // U rows 16wv..16wv+15 = X Z (two accumulator chains, even and odd j)
+    f32x4v ua0 = {0.f, 0.f, 0.f, 0.f}, ua1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float* zb = Zs + (16 * j + 4 * g4) * kUP + l16;
-      uacc = mfma4(f.x[j].x, zb[0], uacc);
-      uacc = mfma4(f.x[j].y, zb[kUP], uacc);
-      uacc = mfma4(f.x[j].z, zb[2 * kUP], uacc);
-      uacc = mfma4(f.x[j].w, zb[3 * kUP], uacc);
+    for (int j = 0; j < 4; j += 2) {
+      const float* z0 = Zs + (16 * j + 4 * g4) * kUP + l16;
+      const float* z1 = z0 + 16 * kUP;
+      ua0 = mfma4(f.x[j].x, z0[0], ua0);
+      ua1 = mfma4(f.x[j + 1].x, z1[0], ua1);
+      ua0 = mfma4(f.x[j].y, z0[kUP], ua0);
+      ua1 = mfma4(f.x[j + 1].y, z1[kUP], ua1);
+      ua0 = mfma4(f.x[j].z, z0[2 * kUP], ua0);
+      ua1 = mfma4(f.x[j + 1].z, z1[2 * kUP], ua1);
+      ua0 = mfma4(f.x[j].w, z0[3 * kUP], ua0);
+      ua1 = mfma4(f.x[j + 1].w, z1[3 * kUP], ua1);
     }
+    const f32x4v uacc = ua0 + ua1;
     fetch_x(nx, f);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wv * 16 + g4 * 4 + i;
       Us[r * kUP + l16] = uacc[i];
-      Uk[r * kUP + l16] = uacc[i] * Ktf[r];
+      Uk[r * kUP + l16] = uacc[i] * Ktf[b][r];
     }
     __syncthreads();
 
-    // y += P U, and out
+    // y += P U (a second chain for odd j), into LDS for the next chunk's flush
+    f32x4v yb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float* ub = Us + (16 * j + 4 * g4) * kUP + l16;
-      yacc = mfma4(f.p[j].x, ub[0], yacc);
-      yacc = mfma4(f.p[j].y, ub[kUP], yacc);
-      yacc = mfma4(f.p[j].z, ub[2 * kUP], yacc);
-      yacc = mfma4(f.p[j].w, ub[3 * kUP], yacc);
+    for (int j = 0; j < 4; j += 2) {
+      const float* u0 = Us + (16 * j + 4 * g4) * kUP + l16;
+      const float* u1 = u0 + 16 * kUP;
+      yacc = mfma4(f.p[j].x, u0[0], yacc);
+      yb = mfma4(f.p[j + 1].x, u1[0], yb);
+      yacc = mfma4(f.p[j].y, u0[kUP], yacc);
+      yb = mfma4(f.p[j + 1].y, u1[kUP], yb);
+      yacc = mfma4(f.p[j].z, u0[2 * kUP], yacc);
+      yb = mfma4(f.p[j + 1].z, u1[2 * kUP], yb);
+      yacc = mfma4(f.p[j].w, u0[3 * kUP], yacc);
+      yb = mfma4(f.p[j + 1].w, u1[3 * kUP], yb);
     }
+    yacc = yacc + yb;
     fetch_p(nx, f);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + wv * 16 + g4 * 4 + i;
-      if (t < n_tokens) yn[(int64_t)t * v_tok + l16] = scale * yacc[i];
-    }
+    for (int i = 0; i < 4; ++i) Ys[(wv * 16 + g4 * 4 + i) * kUP + l16] = scale * yacc[i];
+    // the next chunk's K, V and factors into the other buffer (its last
+    // readers finished before this chunk's first barrier), then its successor
+    stage(b ^ 1, f);
+    fetch_kv(nx2, f);
     // state update of this wave's column tiles: M = gamma_C M + (diag(Ktf) U)^T K
-    const float gam_c = Gam[C - 1];
+    // (the two column tiles interleaved: two chains sharing their A operand)
+    const float gam_c = Gam[b][C - 1];
+    const int col0 = wv * 32 + l16;
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      const int col = (wv * 2 + c2) * 16 + l16;
+    for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
       for (int i = 0; i < 4; ++i) macc[c2][i] *= gam_c;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int s0 = 16 * j + 4 * g4;
-        const float* ua = Uk + s0 * kUP + l16;
-        const float* kb = Ks + s0 * kKSP + col;
-        macc[c2] = mfma4(ua[0], kb[0], macc[c2]);
-        macc[c2] = mfma4(ua[kUP], kb[kKSP], macc[c2]);
-        macc[c2] = mfma4(ua[2 * kUP], kb[2 * kKSP], macc[c2]);
-        macc[c2] = mfma4(ua[3 * kUP], kb[3 * kKSP], macc[c2]);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int s0 = 16 * j + 4 * g4;
+      const float* ua = Uk + s0 * kUP + l16;
+      const float* kb = Ks[b] + s0 * kKSP + col0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Ms[(g4 * 4 + i) * kMP + col] = macc[c2][i];
+      for (int c = 0; c < 4; ++c) {
+        const float a = ua[c * kUP];
+        macc[0] = mfma4(a, kb[c * kKSP], macc[0]);
+        macc[1] = mfma4(a, kb[c * kKSP + 16], macc[1]);
+      }
     }
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Ms[(g4 * 4 + i) * kMP + col0 + 16 * c2] = macc[c2][i];
     __syncthreads();
   }
+  flush_y(n_chunks - 1);
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
