@@ -22,7 +22,9 @@
 //                     would lose ~1e-4), K K^T and Q K^T (lower tiles, MFMA),
 //                     A and P, X blockwise (16 x 16 diagonal tiles by forward
 //                     substitution, the others by MFMA). Writes gamma,
-//                     gamma_C/gamma, beta, X and P to the workspace.
+//                     gamma_C/gamma, beta, X and P to the workspace. Q is read
+//                     as register fragments and K's LDS region is reused for
+//                     A and X, so a block needs ~39 KB (four per CU).
 //  chunk_scan_kernel  one block per (sequence, V-head, 16 state rows), the
 //                     chunks in order: the 16 rows stay on chip, and per chunk
 //                     each of the 4 waves does 128 MFMAs (K M^T and Q M^T,
@@ -86,7 +88,7 @@ __device__ __forceinline__ ChunkUnit chunk_unit(float* ws, int64_t unit) {
 // ---------------------------------------------------------------------------
 // Chunk preparation
 // ---------------------------------------------------------------------------
-constexpr int kKP = kChS + 4;   // LDS row pitch of K and Q (floats)
+constexpr int kKP = kChS + 4;   // LDS row pitch of K (floats)
 constexpr int kAP = kChC + 4;   // LDS row pitch of A and X
 constexpr int kTP = 16 + 4;     // LDS row pitch of a 16 x 16 scratch tile
 
@@ -96,14 +98,17 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     int n_v_heads, int n_chunks) {
   constexpr int S = kChS, C = kChC;
   constexpr int AXT = 2 * C * kAP + 3 * 16 * kTP;   // A, X and three scratch tiles
-  constexpr int QS = (C * kKP > AXT) ? C * kKP : AXT;
-  __shared__ float Ks[C * kKP];
-  __shared__ float Qs[QS];        // reused for A and X once Q K^T is done
+  constexpr int SM = (C * kKP > AXT) ? C * kKP : AXT;
+  // One LDS region: K during the Gram tiles, then A, X and the scratch tiles.
+  // Q never goes through LDS (the Q K^T waves take their rows as register
+  // fragments), which keeps a block at ~39 KB: four blocks per CU.
+  __shared__ float Sm[SM];
   __shared__ double Gs[C];        // Gc in fp64: differences of large sums keep their precision
   __shared__ float Bs[C];
-  float* As = Qs;                 // [C][kAP]
-  float* Xs = Qs + C * kAP;       // [C][kAP]
-  float* Ts = Qs + 2 * C * kAP;   // [3][16][kTP]
+  float* Ks = Sm;                 // [C][kKP]
+  float* As = Sm;                 // [C][kAP]
+  float* Xs = Sm + C * kAP;       // [C][kAP]
+  float* Ts = Sm + 2 * C * kAP;   // [3][16][kTP]
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t unit = blockIdx.x;                    // (n * H + h) * n_chunks + c
@@ -118,16 +123,42 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
   const float* qn = q + (n * n_tokens) * kq_tok + (int64_t)kh * S;
   ChunkUnit u = chunk_unit(ws, unit);
 
-  // K and Q of the chunk (zero past the end)
+  // Gram tiles (lower tiles only, ti >= tj): the Q-waves (0, 1) compute
+  // Q K^T, the K-waves (2, 3) K K^T, each on the tiles of two tile rows,
+  // {0, 3} (even waves) or {1, 2} (odd waves): five tiles per wave.
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const bool qwave = wv < 2;
+  const int par = wv & 1;
+  auto tile_at = [&](int m, int& ti, int& tj) {
+    if (par == 0) {
+      ti = m == 0 ? 0 : 3;
+      tj = m == 0 ? 0 : m - 1;
+    } else {
+      ti = m < 2 ? 1 : 2;
+      tj = m < 2 ? m : m - 2;
+    }
+  };
+  // Q rows of the two tile rows as A fragments (k = 16j + 4*(l/16) + c),
+  // loaded first; rows past the end read the last position (their P rows are
+  // never used: those y are not stored)
+  float4 qa[8], qb[8];
+  if (qwave) {
+    const int last = n_tokens - 1;
+    const int ta = t0 + (par ? 1 : 0) * 16 + l16, tb = t0 + (par ? 2 : 3) * 16 + l16;
+    const float* qra = qn + (int64_t)(ta < last ? ta : last) * kq_tok + 4 * g4;
+    const float* qrb = qn + (int64_t)(tb < last ? tb : last) * kq_tok + 4 * g4;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      qa[j] = load4(qra + 16 * j);
+      qb[j] = load4(qrb + 16 * j);
+    }
+  }
+  // K of the chunk (zero past the end)
   for (int f = tid * 4; f < C * S; f += 256 * 4) {
     const int t = f / S, col = f % S;
-    float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
-    if (t0 + t < n_tokens) {
-      kv = load4(kn + (int64_t)(t0 + t) * kq_tok + col);
-      qv = load4(qn + (int64_t)(t0 + t) * kq_tok + col);
-    }
+    float4 kv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t0 + t < n_tokens) kv = load4(kn + (int64_t)(t0 + t) * kq_tok + col);
     store4(Ks + t * kKP + col, kv);
-    store4(Qs + t * kKP + col, qv);
   }
   // cumulative log-decay (inclusive prefix sum across wave 0) and beta
   if (wv == 0) {
@@ -150,48 +181,51 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     u.bet[tid] = Bs[tid];
   }
 
-  // K K^T and Q K^T on the lower tiles (ti >= tj): 10 tiles each, 20 per
-  // block, 5 per wave (tile id = wv + 4m: ids 0..9 are K K^T, 10..19 Q K^T)
-  const int g4 = lane >> 4, l16 = lane & 15;
-  auto tile_of = [](int idx, int& ti, int& tj) {   // idx % 10 -> (ti >= tj)
-    const int tix = idx % 10;
-    ti = (tix >= 1) + (tix >= 3) + (tix >= 6);
-    tj = tix - ti * (ti + 1) / 2;
-  };
   f32x4v acc5[5];
 #pragma unroll
   for (int m = 0; m < 5; ++m) {
-    const int idx = wv + 4 * m;
     int ti, tj;
-    tile_of(idx, ti, tj);
-    const float* Arow = (idx < 10 ? Ks : Qs) + (ti * 16 + l16) * kKP + g4 * (S / 4);
-    const float* Brow = Ks + (tj * 16 + l16) * kKP + g4 * (S / 4);
+    tile_at(m, ti, tj);
+    const float* Brow = Ks + (tj * 16 + l16) * kKP + 4 * g4;
     f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+    if (qwave) {
+      const bool first_row = (par == 0) ? (m == 0) : (m < 2);
 #pragma unroll
-    for (int kk = 0; kk < S / 4; kk += 4) {
-      const float4 a4 = load4(Arow + kk);
-      const float4 b4 = load4(Brow + kk);
-      acc = mfma4(a4.x, b4.x, acc);
-      acc = mfma4(a4.y, b4.y, acc);
-      acc = mfma4(a4.z, b4.z, acc);
-      acc = mfma4(a4.w, b4.w, acc);
+      for (int j = 0; j < 8; ++j) {
+        const float4 a4 = first_row ? qa[j] : qb[j];
+        const float4 b4 = load4(Brow + 16 * j);
+        acc = mfma4(a4.x, b4.x, acc);
+        acc = mfma4(a4.y, b4.y, acc);
+        acc = mfma4(a4.z, b4.z, acc);
+        acc = mfma4(a4.w, b4.w, acc);
+      }
+    } else {
+      const float* Arow = Ks + (ti * 16 + l16) * kKP + 4 * g4;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float4 a4 = load4(Arow + 16 * j);
+        const float4 b4 = load4(Brow + 16 * j);
+        acc = mfma4(a4.x, b4.x, acc);
+        acc = mfma4(a4.y, b4.y, acc);
+        acc = mfma4(a4.z, b4.z, acc);
+        acc = mfma4(a4.w, b4.w, acc);
+      }
     }
     acc5[m] = acc;
   }
-  __syncthreads();   // Q no longer needed: As and Xs overwrite Qs
+  __syncthreads();   // K no longer needed: A and X overwrite it
 #pragma unroll
   for (int m = 0; m < 5; ++m) {
-    const int idx = wv + 4 * m;
     int ti, tj;
-    tile_of(idx, ti, tj);
+    tile_at(m, ti, tj);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = ti * 16 + g4 * 4 + i, s = tj * 16 + l16;
       const float r = expf((float)(Gs[t] - Gs[s]));
-      if (idx < 10) {
-        As[t * kAP + s] = (s < t) ? Bs[t] * r * acc5[m][i] : 0.0f;
-      } else {
+      if (qwave) {
         u.p[frag_index(t, s, 4)] = (s <= t) ? r * acc5[m][i] : 0.0f;
+      } else {
+        As[t * kAP + s] = (s < t) ? Bs[t] * r * acc5[m][i] : 0.0f;
       }
     }
   }
