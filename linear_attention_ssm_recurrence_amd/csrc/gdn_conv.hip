@@ -61,7 +61,6 @@ __global__ __launch_bounds__(256) void conv_scan_kernel(const float* __restrict_
   const int c = cb * 256 + threadIdx.x;
   if (c >= conv_dim) return;
   const int t0 = chunk * TB;
-  const int t1 = min(t0 + TB, n_tokens);
   const float* xc = x + n * (int64_t)n_tokens * conv_dim + c;
   float* oc = out + n * (int64_t)n_tokens * conv_dim + c;
   float* cs = conv_state + (n * conv_dim + c) * (K - 1);
@@ -87,16 +86,27 @@ __global__ __launch_bounds__(256) void conv_scan_kernel(const float* __restrict_
       fin[u] = t < 0 ? cs[K - 1 + t] : xc[(int64_t)t * conv_dim];
     }
   }
-  for (int t = t0; t < t1; ++t) {
-    const float xv = xc[(int64_t)t * conv_dim];
-    oc[(int64_t)t * conv_dim] = conv_point<K>(xv, hist, wc);
+  // every input of the chunk loaded before any arithmetic, so the loads are
+  // in flight together (positions past the end read the last one, unused)
+  float xs[TB];
+#pragma unroll
+  for (int i = 0; i < TB; ++i) {
+    const int t = t0 + i < n_tokens ? t0 + i : n_tokens - 1;
+    xs[i] = xc[(int64_t)t * conv_dim];
+  }
+#pragma unroll
+  for (int i = 0; i < TB; ++i) {
+    const int t = t0 + i;
+    if (t < n_tokens) oc[(int64_t)t * conv_dim] = conv_point<K>(xs[i], hist, wc);
 #pragma unroll
     for (int u = 0; u + 1 < K - 1; ++u) hist[u] = hist[u + 1];
-    hist[K - 2] = xv;
+    hist[K - 2] = xs[i];
     if constexpr (SNAP) {
-      float* sn = snaps + ((n * n_tokens + t) * conv_dim + c) * (K - 1);
+      if (t < n_tokens) {
+        float* sn = snaps + ((n * n_tokens + t) * conv_dim + c) * (K - 1);
 #pragma unroll
-      for (int u = 0; u < K - 1; ++u) sn[u] = hist[u];
+        for (int u = 0; u < K - 1; ++u) sn[u] = hist[u];
+      }
     }
   }
   if (chunk == 0) {
