@@ -61,6 +61,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN decode state GB/s (% HBM peak) @32h S=128; scan tokens/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor specification
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, vendor specification
+FP32_MFMA_PEAK_TFLOPS = 157.3    # MI355X dense fp32 matrix, vendor specification
 
 
 def log(*a):
@@ -270,10 +271,23 @@ def run_scan(torch, gdn, inputs, steps, warmup):
         "scan_algorithmic_bytes": scan_bytes,
         "chunked_scan_ms": t_chunk.event_ms / steps,
         "chunked_scan_tokens_per_s": N * T / (t_chunk.event_ms / steps * 1e-3),
+        "chunked_mfma_TFLOPs": chunked_mfma_flops(N, T, H) / (t_chunk.event_ms / steps * 1e-3) / 1e12,
+        "chunked_frac_fp32_mfma_peak": chunked_mfma_flops(N, T, H) / (t_chunk.event_ms / steps * 1e-3)
+                                       / 1e12 / FP32_MFMA_PEAK_TFLOPS,
         "conv_kernel_ms": conv_ms,
         "conv_GBps": conv_bytes / (conv_ms * 1e-3) / 1e9,
         "conv_frac_hbm_peak": conv_bytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
     }
+
+
+def chunked_mfma_flops(N, T, H) -> float:
+    """fp32 MFMA work of one chunked scan at S = 128 (v_mfma_f32_16x16x4f32,
+    2048 flop each): per 64-position chunk and head, the preparation runs 704
+    (20 Gram tiles x 32, 64 for the blockwise inverse) and the scan's 8 row
+    blocks x 4 waves run 128 each."""
+    chunks = (T + 63) // 64
+    per_head_chunk = 704 + 8 * 4 * 128
+    return 2048.0 * N * H * chunks * per_head_chunk
 
 
 def run_spec(torch, gdn, inputs, steps, warmup):
