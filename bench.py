@@ -539,7 +539,7 @@ def run_block(torch, gdn, inputs, steps, warmup):
 
 
 DECODE_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "recurrence_decode_256x32x128_traffic.md")
-DECODE_SOURCES = ("linear_attention_ssm_recurrence_amd/csrc/gdn_recurrence.hip",
+DECODE_SOURCES = ("linear_attention_ssm_recurrence_amd/csrc/gdn_decode.hpp",
                   "linear_attention_ssm_recurrence_amd/csrc/gdn_device.hpp")
 
 
