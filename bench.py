@@ -280,6 +280,11 @@ def run_scan(torch, gdn, inputs, steps, warmup):
     }
 
 
+def w_scan_tokens(leg) -> float:
+    """Tokens per step of the scan leg (conv + scan over one 4096-token sequence)."""
+    return leg["tokens_per_s"] * leg["ms_per_step"] * 1e-3
+
+
 def chunked_mfma_flops(N, T, H) -> float:
     """fp32 MFMA work of one chunked scan at S = 128 (v_mfma_f32_16x16x4f32,
     2048 flop each): per 64-position chunk and head, the preparation runs 704
@@ -712,6 +717,10 @@ def main():
         line["copy_calibration"] = line_copy
     if "scan" in out_legs:
         line["scan_tokens_per_s"] = out_legs["scan"]["tokens_per_s"]
+        line["scan_tokens_per_s_note"] = ("conv1d+SiLU then the chunked scan; the sequential scan "
+                                          "(VALU) is scan_sequential_tokens_per_s")
+        line["scan_sequential_tokens_per_s"] = (
+            w_scan_tokens(out_legs["scan"]) / (out_legs["scan"]["sequential_ms_per_step"] * 1e-3))
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {host_threads()} threads, ~{args.cpu_seconds:.0f} s")
         line["cpu_baseline"] = cpu_baseline(inputs, d, args.cpu_seconds)
