@@ -30,9 +30,10 @@
 //                     each of the 4 waves does 128 MFMAs (K M^T and Q M^T,
 //                     X Z, P U, the state update).
 // Positions past the end of the sequence in the last chunk are padded with
-// g = 0, beta = 0 and k = q = 0 in the preparation: their rows of A, X Z and
-// U, and their entries of beta, are zero, so they leave the state unchanged,
-// and their y are not stored.
+// g = 0, beta = 0 and k = 0 in the preparation: their rows of A, X Z and U,
+// and their entries of beta, are zero, so they leave the state unchanged.
+// Their q (read from the last valid position) only reaches their own rows of
+// P and y, and those y are not stored.
 //
 // MFMA v_mfma_f32_16x16x4f32 (checked on MI355X): lane l supplies
 // A[l%16][l/16] and B[l/16][l%16]; output element i of lane l is
