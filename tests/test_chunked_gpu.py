@@ -78,3 +78,65 @@ def test_chunked_scan_4096():
     y, st = _gpu_chunked(p, w.scale)
     assert_close(host(y), y_ref, "chunked y T=4096", rtol=RTOL_LONG_SCAN)
     assert_close(host(st), st_ref, "chunked state T=4096", rtol=RTOL_LONG_SCAN)
+
+
+def _slice(p, a, b):
+    """Positions a..b-1 of a case (the state is the case's initial state)."""
+    out = {key: np.ascontiguousarray(val[:, a:b]) for key, val in p.items() if key != "state"}
+    out["state"] = p["state"]
+    return out
+
+
+def test_chunked_split_resume():
+    """Two chunked calls (T1 then T2, both splits inside a chunk) carry the
+    state exactly like one sequential pass over T1 + T2 (oracle)."""
+    rng = np.random.default_rng(901)
+    N, T1, T2, HK, H = 2, 100, 91, 2, 4
+    p = _case(rng, N, T1 + T2, HK, H)
+    scale = 1 / math.sqrt(128)
+    y_ref, st_ref = oracle.recurrence_seq(p["state"], p["q"], p["k"], p["v"], p["g"], p["beta"],
+                                          scale)
+    y1, st1 = _gpu_chunked(_slice(p, 0, T1), scale)
+    p2 = _slice(p, T1, T1 + T2)
+    p2["state"] = host(st1)
+    y2, st2 = _gpu_chunked(p2, scale)
+    assert_close(np.concatenate([host(y1), host(y2)], axis=1), y_ref, "chunked split/resume y")
+    assert_close(host(st2), st_ref, "chunked split/resume state")
+
+
+def test_chunked_many_blocks_gqa():
+    """6 sequences x 300 positions, 8 -> 32 heads: 1536 scan blocks (several
+    per CU, XCD grouping over many heads), ragged last chunk."""
+    rng = np.random.default_rng(902)
+    N, T, HK, H = 6, 300, 8, 32
+    p = _case(rng, N, T, HK, H)
+    scale = 1 / math.sqrt(128)
+    y_ref, st_ref = oracle.recurrence_seq(p["state"], p["q"], p["k"], p["v"], p["g"], p["beta"],
+                                          scale)
+    y, st = _gpu_chunked(p, scale)
+    assert_close(host(y), y_ref, "chunked 6x300 y")
+    assert_close(host(st), st_ref, "chunked 6x300 state")
+
+
+def test_chunked_vs_sequential_gpu_prefill_shape():
+    """The prefill's shape (1 x 4096, 16 -> 32 heads, nonzero start state):
+    the chunked scan against the sequential GPU scan on every head, and
+    against the oracle on two sampled heads, within the long-scan tolerance."""
+    rng = np.random.default_rng(903)
+    N, T, HK, H = 1, 4096, 16, 32
+    p = _case(rng, N, T, HK, H)
+    scale = 1 / math.sqrt(128)
+    y_c, st_c = _gpu_chunked(p, scale)
+    st_s = dev(p["state"])
+    y_s = torch.empty_like(y_c)
+    gdn.gdn_recurrence_seq_ex(st_s, dev(p["qh"]), dev(p["kh"]), dev(p["v"]), dev(p["g"]),
+                              dev(p["beta"]), y_s, scale)
+    assert_close(host(y_c), host(y_s), "chunked vs sequential y", rtol=RTOL_LONG_SCAN)
+    assert_close(host(st_c), host(st_s), "chunked vs sequential state", rtol=RTOL_LONG_SCAN)
+    heads = [0, 31]                       # K-heads 0 and 15
+    sub = lambda x: np.ascontiguousarray(x[:, :, heads])
+    y_ref, st_ref = oracle.recurrence_seq(np.ascontiguousarray(p["state"][:, heads]), sub(p["q"]),
+                                          sub(p["k"]), sub(p["v"]), sub(p["g"]), sub(p["beta"]),
+                                          scale)
+    assert_close(host(y_c)[:, :, heads], y_ref, "chunked y, sampled heads", rtol=RTOL_LONG_SCAN)
+    assert_close(host(st_c)[:, heads], st_ref, "chunked state, sampled heads", rtol=RTOL_LONG_SCAN)
