@@ -1,0 +1,60 @@
+"""Every entry point enqueues on the stream the caller passes (needs an MI355X).
+
+The decode, the scan and the fused layer are run on a side stream (with the
+default stream busy on other work) and on the default stream; the results
+must be identical bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import DEV, dev, prep_recurrence
+from linear_attention_ssm_recurrence_amd import gdn, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdn.load_library()
+
+
+def _bits(x):
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(DEV)
+
+
+def test_side_stream_equals_default_stream():
+    w = inputs.WORKLOADS[0]
+    d = inputs.draw(w)
+    p = prep_recurrence(d, w)
+    wb = inputs.WORKLOADS[4]
+    lb = inputs.draw_block_layer(1, wb, n_seqs=4)
+    H, HK, S = wb.n_v_heads, wb.n_k_heads, wb.state_size
+
+    def run(stream):
+        st_scan = dev(p["state"])
+        y_scan = torch.empty(p["v"].shape, device=DEV)
+        b_in = {key: (_bits(val) if val.dtype == np.uint16 else dev(val)) for key, val in lb.items()}
+        out = torch.empty((4, H, S), device=DEV)
+        with torch.cuda.stream(stream):
+            gdn.gdn_recurrence_seq(st_scan, dev(p["q"]), dev(p["k"]), dev(p["v"]), dev(p["g"]),
+                                   dev(p["beta"]), y_scan, w.scale)
+            gdn.gdn_decode_block_bf16(b_in["qkv"], b_in["z"], b_in["a"], b_in["b"],
+                                      b_in["conv_w"], b_in["A_log"], b_in["dt_bias"],
+                                      b_in["norm_w"], b_in["conv_state"], b_in["state"], out, HK,
+                                      wb.scale, wb.l2_eps, wb.eps)
+        stream.synchronize()
+        return st_scan, y_scan, b_in["state"], b_in["conv_state"], out
+
+    torch.cuda.synchronize()
+    ref = run(torch.cuda.current_stream())
+    side = torch.cuda.Stream()
+    busy = torch.randn(1 << 22, device=DEV)
+    for _ in range(20):                       # keep the default stream busy meanwhile
+        busy.mul_(1.0001)
+    got = run(side)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
