@@ -304,8 +304,8 @@ size_t gdn_chunked_workspace_bytes(int n_seqs, int n_tokens, int n_v_heads, int 
  * aligned; contents on return unspecified). y and the state agree with the
  * sequential scan within the fp32 tolerance, not bit for bit.
  * Errors: GDN_ENULL; GDN_ESIZE (as gdn_recurrence_seq_ex, or workspace too
- * small); GDN_EUNSUPPORTED (state_size != 128); GDN_EALIGN (state, q, k, v or
- * workspace not 16-byte aligned); GDN_ELAUNCH.
+ * small); GDN_EUNSUPPORTED (state_size != 128); GDN_EALIGN (state, q, k, v, y
+ * or workspace not 16-byte aligned); GDN_ELAUNCH.
  */
 int gdn_recurrence_seq_chunked(float *state, const float *q, const float *k, const float *v,
                                const float *g, const float *beta, float *y, void *workspace,

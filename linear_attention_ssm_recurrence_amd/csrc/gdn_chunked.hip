@@ -574,7 +574,8 @@ extern "C" int gdn_recurrence_seq_chunked(float* state, const float* q, const fl
   if (!state || !q || !k || !v || !g || !beta || !y || !workspace) return GDN_ENULL;
   const size_t need = gdn_chunked_workspace_bytes(n_seqs, n_tokens, n_v_heads, state_size);
   if (workspace_bytes < need) return GDN_ESIZE;
-  if (!aligned16(state) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(workspace))
+  if (!aligned16(state) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y) ||
+      !aligned16(workspace))
     return GDN_EALIGN;
   const int n_chunks = (n_tokens + kChC - 1) / kChC;
   const int64_t units = (int64_t)n_seqs * n_v_heads * n_chunks;

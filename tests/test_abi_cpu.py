@@ -212,8 +212,8 @@ def test_chunked_validation(lib):
     assert need == 1 * 4 * 2 * 8448 * 4
     assert lib.gdn_chunked_workspace_bytes(1, 100, 4, 64) == 0
 
-    def call(state=FAKE, ws=FAKE, ws_bytes=need, T=100, HK=2, H=4, S=128):
-        return f(state, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, ws_bytes, 1, T, HK, H, S, 0.1, NUL)
+    def call(state=FAKE, ws=FAKE, ws_bytes=need, T=100, HK=2, H=4, S=128, y=FAKE):
+        return f(state, FAKE, FAKE, FAKE, FAKE, FAKE, y, ws, ws_bytes, 1, T, HK, H, S, 0.1, NUL)
 
     assert call(state=NUL) == gdn.GDN_ENULL
     assert call(ws=NUL) == gdn.GDN_ENULL
@@ -222,6 +222,7 @@ def test_chunked_validation(lib):
     assert call(HK=3) == gdn.GDN_ESIZE
     assert call(state=FAKE_MIS) == gdn.GDN_EALIGN
     assert call(ws=FAKE_MIS) == gdn.GDN_EALIGN
+    assert call(y=FAKE_MIS) == gdn.GDN_EALIGN
     assert call(state=NUL, ws=NUL, T=0) == gdn.GDN_OK
 
 
