@@ -121,3 +121,51 @@ def test_conv_snapshots(K, T):
     full = np.concatenate([cs0, np.transpose(x, (0, 2, 1))], axis=2)   # [N][C][K-1+T]
     for t in range(T):
         assert np.array_equal(sn[:, t], full[:, :, t + 1:t + K]), f"conv snapshot {t}"
+
+
+def test_t4_full_batch():
+    """The bench's decode_t4 shape (256 x 32 x 128, q/k per K-head): the T4
+    read-out leaves the state bit-identical to the exact read-out, and its y
+    agrees with the exact y (which the full-batch parity test checks against
+    the oracle) within the tolerance."""
+    rng = np.random.default_rng(1700)
+    N, HK, H, S = 256, 16, 32, 128
+    qh = oracle.l2norm_gqa(rng.standard_normal((N, HK, S)), HK)
+    kh = oracle.l2norm_gqa(rng.standard_normal((N, HK, S)), HK)
+    v = rng.standard_normal((N, H, S)).astype(np.float32)
+    g = oracle.decay_gate(rng.standard_normal((N, H)), np.zeros(H), rng.standard_normal(H))
+    beta = oracle.sigmoid(rng.standard_normal((N, H)))
+    st0 = (rng.standard_normal((N, H, S, S)) * 0.05).astype(np.float32)
+    scale = 1 / math.sqrt(S)
+    out = []
+    for variant in (gdn.GDN_RECUR_EXACT, gdn.GDN_RECUR_T4):
+        st = dev(st0)
+        y = torch.empty((N, H, S), device=DEV)
+        gdn.gdn_recurrence_ex(st, dev(qh), dev(kh), dev(v), dev(g), dev(beta), y, scale, variant)
+        out.append((st, y))
+    assert torch.equal(out[0][0], out[1][0]), "T4 changed the state"
+    assert_close(host(out[1][1]), host(out[0][1]), "T4 y vs exact y, full batch")
+
+
+def test_spec_verify_shape_snapshots():
+    """The bench's speculative-verify shape (64 sequences x 4 tokens, 16 -> 32
+    heads, S = 128): snapshot t equals the state after t + 1 decode launches,
+    bit for bit, and the y of each token equals that launch's y."""
+    rng = np.random.default_rng(1701)
+    N, T, HK, H, S = 64, 4, 16, 32, 128
+    p = _inputs(rng, N, T, HK, H, S)
+    scale = 1 / math.sqrt(S)
+    st = dev(p["state"])
+    y = torch.empty((N, T, H, S), device=DEV)
+    snaps = torch.full((N, T, H, S, S), float("nan"), device=DEV)
+    gdn.gdn_recurrence_seq_ex(st, dev(p["qh"]), dev(p["kh"]), dev(p["v"]), dev(p["g"]),
+                              dev(p["beta"]), y, scale, snaps)
+    st_d = dev(p["state"])
+    for t in range(T):
+        y_d = torch.empty((N, H, S), device=DEV)
+        sl = lambda x: dev(np.ascontiguousarray(x[:, t]))
+        gdn.gdn_recurrence_ex(st_d, sl(p["qh"]), sl(p["kh"]), sl(p["v"]), sl(p["g"]),
+                              sl(p["beta"]), y_d, scale, gdn.GDN_RECUR_EXACT)
+        assert torch.equal(snaps[:, t], st_d), f"snapshot {t} != state after {t + 1} launches"
+        assert torch.equal(y[:, t], y_d), f"y of token {t} != decode launch {t}"
+    assert torch.equal(st, st_d)
