@@ -317,7 +317,7 @@ struct ChunkRegs {
   float gam, ktf, bet;
 };
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
                        const float* __restrict__ k, const float* __restrict__ v,
                        const float* __restrict__ ws, float* __restrict__ y, int n_tokens,
@@ -328,14 +328,15 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
   __shared__ float Us[C * kUP];   // U
   __shared__ float Uk[C * kUP];   // diag(gamma_C / gamma) U, for the state update
   __shared__ float Ys[C * kUP];   // y of the chunk, stored after the chunk's last barrier
-  // K, V and the factors of a chunk, double-buffered: chunk c + 1's copy is
-  // written during chunk c, so a chunk needs three barriers (after Z, after
-  // U, at the end), not four
-  __shared__ float Vs[2][C * kUP];
-  __shared__ float Ks[2][C * kKSP];
-  __shared__ float Gam[2][C];     // gamma_t
-  __shared__ float Ktf[2][C];     // gamma_C / gamma_s
-  __shared__ float Bet[2][C];     // beta_t
+  // K, V and the factors of the chunk, staged at the top of each chunk. One
+  // buffer keeps the block at ~69 KB of LDS, so two blocks share a CU when
+  // there are more blocks than CUs (their waves are not tied by barriers);
+  // a second buffer (one barrier less per chunk) measured no faster.
+  __shared__ float Vs[C * kUP];
+  __shared__ float Ks[C * kKSP];
+  __shared__ float Gam[C];        // gamma_t
+  __shared__ float Ktf[C];        // gamma_C / gamma_s
+  __shared__ float Bet[C];        // beta_t
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
@@ -404,18 +405,18 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
 #pragma unroll
     for (int i = 0; i < 4; ++i) macc[c2][i] = Ms[(g4 * 4 + i) * kMP + (wv * 2 + c2) * 16 + l16];
 
-  // K, V and the factors of a chunk from registers into LDS buffer b
-  auto stage = [&](int b, const ChunkRegs& f) {
+  // K, V and the factors of a chunk from registers into LDS
+  auto stage = [&](const ChunkRegs& f) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int fi = (j * 256 + tid) * 4;
-      store4(Ks[b] + (fi / S) * kKSP + fi % S, f.kst[j]);
+      store4(Ks + (fi / S) * kKSP + fi % S, f.kst[j]);
     }
-    store4(Vs[b] + (tid >> 2) * kUP + (tid & 3) * 4, f.v);
+    store4(Vs + (tid >> 2) * kUP + (tid & 3) * 4, f.v);
     if (wv == 0) {
-      Gam[b][lane] = f.gam;
-      Ktf[b][lane] = f.ktf;
-      Bet[b][lane] = f.bet;
+      Gam[lane] = f.gam;
+      Ktf[lane] = f.ktf;
+      Bet[lane] = f.bet;
     }
   };
   // y rows of chunk c from LDS to memory, a float4 per thread: each wave
@@ -432,20 +433,19 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
   fetch_q(0, f);
   fetch_x(0, f);
   fetch_p(0, f);
-  stage(0, f);
-  fetch_kv(n_chunks > 1 ? 1 : 0, f);
-  __syncthreads();
 
   for (int chunk = 0; chunk < n_chunks; ++chunk) {
-    const int b = chunk & 1;
     const int nx = chunk + 1 < n_chunks ? chunk + 1 : chunk;   // last chunk: harmless re-read
-    const int nx2 = chunk + 2 < n_chunks ? chunk + 2 : n_chunks - 1;
     if (chunk > 0) flush_y(chunk - 1);
+    // stage this chunk's K, V and factors, then start loading the next chunk's
+    stage(f);
+    fetch_kv(nx, f);
+    __syncthreads();
 
     // rows 16wv..16wv+15 of K M^T and Q M^T (K from LDS, q from registers)
     f32x4v zacc = {0.f, 0.f, 0.f, 0.f}, yacc = {0.f, 0.f, 0.f, 0.f};
     const float* mr = Ms + l16 * kMP + 4 * g4;
-    const float* kr = Ks[b] + trow * kKSP + 4 * g4;
+    const float* kr = Ks + trow * kKSP + 4 * g4;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float4 m4 = load4(mr + 16 * j);
@@ -463,8 +463,8 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wv * 16 + g4 * 4 + i;   // position of output element i
-      const float bt = Bet[b][r], gm = Gam[b][r];
-      Zs[r * kUP + l16] = bt * Vs[b][r * kUP + l16] - (bt * gm) * zacc[i];
+      const float bt = Bet[r], gm = Gam[r];
+      Zs[r * kUP + l16] = bt * Vs[r * kUP + l16] - (bt * gm) * zacc[i];
       yacc[i] *= gm;                         // diag(gamma) Q M^T
     }
     __syncthreads();
@@ -490,7 +490,7 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
     for (int i = 0; i < 4; ++i) {
       const int r = wv * 16 + g4 * 4 + i;
       Us[r * kUP + l16] = uacc[i];
-      Uk[r * kUP + l16] = uacc[i] * Ktf[b][r];
+      Uk[r * kUP + l16] = uacc[i] * Ktf[r];
     }
     __syncthreads();
 
@@ -513,13 +513,9 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
     fetch_p(nx, f);
 #pragma unroll
     for (int i = 0; i < 4; ++i) Ys[(wv * 16 + g4 * 4 + i) * kUP + l16] = scale * yacc[i];
-    // the next chunk's K, V and factors into the other buffer (its last
-    // readers finished before this chunk's first barrier), then its successor
-    stage(b ^ 1, f);
-    fetch_kv(nx2, f);
     // state update of this wave's column tiles: M = gamma_C M + (diag(Ktf) U)^T K
     // (the two column tiles interleaved: two chains sharing their A operand)
-    const float gam_c = Gam[b][C - 1];
+    const float gam_c = Gam[C - 1];
     const int col0 = wv * 32 + l16;
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
@@ -529,7 +525,7 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
     for (int j = 0; j < 4; ++j) {
       const int s0 = 16 * j + 4 * g4;
       const float* ua = Uk + s0 * kUP + l16;
-      const float* kb = Ks[b] + s0 * kKSP + col0;
+      const float* kb = Ks + s0 * kKSP + col0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const float a = ua[c * kUP];
