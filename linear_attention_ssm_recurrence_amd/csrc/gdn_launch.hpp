@@ -41,6 +41,21 @@ inline unsigned grid_for(int64_t items, int per_block) {
   return (unsigned)((items + per_block - 1) / per_block);
 }
 
+// Compute units of the current device (queried once per device; 256 on
+// MI355X). Used only to choose between launch shapes, never for correctness.
+inline int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 // The dispatcher hands workgroup b to XCD b % 8. This maps a block id to a
 // logical block so that consecutive logical blocks share an XCD (and its L2),
 // when the grid divides evenly.

@@ -169,3 +169,29 @@ def test_spec_verify_shape_snapshots():
         assert torch.equal(snaps[:, t], st_d), f"snapshot {t} != state after {t + 1} launches"
         assert torch.equal(y[:, t], y_d), f"y of token {t} != decode launch {t}"
     assert torch.equal(st, st_d)
+
+
+def test_scan_many_blocks_short_chunks():
+    """3 sequences x 70 tokens, 8 -> 32 heads, S = 128: 768 scan blocks, more
+    than the CUs, which selects the 32-token chunk variant of the scan. It
+    must match the oracle, and equal chained decode launches bit for bit."""
+    rng = np.random.default_rng(1702)
+    N, T, HK, H, S = 3, 70, 8, 32, 128
+    p = _inputs(rng, N, T, HK, H, S)
+    scale = 1 / math.sqrt(S)
+    y_ref, st_ref = oracle.recurrence_seq(p["state"], p["q"], p["k"], p["v"], p["g"], p["beta"],
+                                          scale)
+    st = dev(p["state"])
+    y = torch.empty((N, T, H, S), device=DEV)
+    gdn.gdn_recurrence_seq_ex(st, dev(p["qh"]), dev(p["kh"]), dev(p["v"]), dev(p["g"]),
+                              dev(p["beta"]), y, scale)
+    assert_close(host(y), y_ref, "scan 768 blocks y")
+    assert_close(host(st), st_ref, "scan 768 blocks state")
+    st_d = dev(p["state"])
+    for t in range(T):
+        y_d = torch.empty((N, H, S), device=DEV)
+        sl = lambda x: dev(np.ascontiguousarray(x[:, t]))
+        gdn.gdn_recurrence_ex(st_d, sl(p["qh"]), sl(p["kh"]), sl(p["v"]), sl(p["g"]),
+                              sl(p["beta"]), y_d, scale, gdn.GDN_RECUR_EXACT)
+        assert torch.equal(y[:, t], y_d), f"token {t}: scan y != decode launch y"
+    assert torch.equal(st, st_d), "scan state != chained decode launches"
