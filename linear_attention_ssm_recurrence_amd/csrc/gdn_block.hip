@@ -13,7 +13,7 @@
 // it every V-head vh = kh + r*HK (r < GQ = H/HK). The conv channels those
 // heads read (q and k of kh, v of each vh) are read by no other workgroup, so
 // each channel's history is rolled exactly once. The workgroup:
-//   0. issues the small loads of phases 1-2 (conv inputs, gate inputs), then
+//   0. issues the small loads of phases 1-2 and 4 (conv, gate and norm inputs), then
 //      the loads of all its state rows (GQ*S rows, 64 KiB per V-head), so
 //      that the state's HBM transfer overlaps phases 1-2 (the hardware
 //      counts outstanding loads in issue order: loads issued after the state
@@ -95,6 +95,19 @@ __global__ __launch_bounds__(64 * kBlockWaves) void decode_block_kernel(
     gb = b[n * n_v_heads + h];
   }
 
+  // 0a'. z and norm_w of the gated norm (waves 0..GQ-1, one float4 group of
+  // the head's row per lane), so that phase 4 waits on no global load: the
+  // next workgroup on this CU needs the slots of waves 0..GQ-1 as well
+  static_assert(S / 4 <= 64, "one float4 group of a norm row per lane");
+  const bool norm_lane = (wv < GQ && lane < S / 4);
+  uint2 zb_pre = make_uint2(0u, 0u);
+  float4 nw_pre = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (norm_lane) {
+    const int h = kh + wv * n_k_heads;
+    zb_pre = *reinterpret_cast<const uint2*>(z + (n * n_v_heads + h) * S + 4 * lane);
+    nw_pre = load4(norm_w + 4 * lane);
+  }
+
   // 0b. state rows of this wave: combined row R = wv*RW + ... over the GQ heads
   const int r_head = (wv * RW) / S;                 // which of the GQ V-heads
   const int vh = kh + r_head * n_k_heads;
@@ -172,12 +185,12 @@ __global__ __launch_bounds__(64 * kBlockWaves) void decode_block_kernel(
     const float* yr = ys + wv * S;
     const float ss = row_sumsq(yr, S / 4, lane);
     const float inv = 1.0f / sqrtf(ss / (float)S + eps);
-    const uint16_t* zr = z + (n * n_v_heads + h) * S;
     float* orow = out + (n * n_v_heads + h) * S;
-    for (int m = lane; m < S / 4; m += 64) {
+    if (norm_lane) {
+      const int m = lane;
       const float4 yv = load4(yr + 4 * m);
-      const float4 wv4 = load4(norm_w + 4 * m);
-      const uint2 zb = *reinterpret_cast<const uint2*>(zr + 4 * m);
+      const float4 wv4 = nw_pre;
+      const uint2 zb = zb_pre;
       const float z0 = bf16_to_float((uint16_t)(zb.x & 0xFFFFu));
       const float z1 = bf16_to_float((uint16_t)(zb.x >> 16));
       const float z2 = bf16_to_float((uint16_t)(zb.y & 0xFFFFu));

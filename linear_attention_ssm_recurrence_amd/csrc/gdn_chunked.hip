@@ -30,10 +30,11 @@
 //                     each of the 4 waves does 128 MFMAs (K M^T and Q M^T,
 //                     X Z, P U, the state update).
 // Positions past the end of the sequence in the last chunk are padded with
-// g = 0, beta = 0 and k = 0 in the preparation: their rows of A, X Z and U,
-// and their entries of beta, are zero, so they leave the state unchanged.
-// Their q (read from the last valid position) only reaches their own rows of
-// P and y, and those y are not stored.
+// g = 0 and beta = 0 in the preparation, and their q and k rows repeat the
+// last valid position: their rows of A, Z and U, and their entries of beta,
+// are zero, so they leave the state unchanged, and a valid row t meets them
+// neither in A nor in P (both take s <= t). Their rows of P and y are not
+// used: those y are not stored.
 //
 // MFMA v_mfma_f32_16x16x4f32 (checked on MI355X): lane l supplies
 // A[l%16][l/16] and B[l/16][l%16]; output element i of lane l is
@@ -154,26 +155,43 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
       qb[j] = load4(qrb + 16 * j);
     }
   }
-  // K of the chunk (zero past the end)
-  for (int f = tid * 4; f < C * S; f += 256 * 4) {
-    const int t = f / S, col = f % S;
-    float4 kv = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t0 + t < n_tokens) kv = load4(kn + (int64_t)(t0 + t) * kq_tok + col);
-    store4(Ks + t * kKP + col, kv);
+  // K of the chunk: all eight float4 loads of a thread are in flight
+  // together. Rows past the end repeat the last position; their beta is 0,
+  // so their rows of A are zero, and no valid row t reads them (A and P use
+  // s <= t).
+  constexpr int KF = C * S / (256 * 4);
+  float4 kv[KF];
+#pragma unroll
+  for (int i = 0; i < KF; ++i) {
+    const int f = (tid + 256 * i) * 4, t = f / S, col = f % S;
+    const int tt = t0 + t < n_tokens ? t0 + t : n_tokens - 1;
+    kv[i] = load4(kn + (int64_t)tt * kq_tok + col);
+  }
+  // g and beta of the chunk (wave 0), issued after K: outstanding loads
+  // complete in issue order, so K's stores below do not wait for them
+  float g_raw = 0.0f, b_raw = 0.0f;
+  if (wv == 0) {
+    const int t = t0 + lane < n_tokens ? t0 + lane : n_tokens - 1;
+    const int64_t gi = (n * n_tokens + t) * n_v_heads + h;
+    g_raw = g[gi];
+    b_raw = beta[gi];
+  }
+#pragma unroll
+  for (int i = 0; i < KF; ++i) {
+    const int f = (tid + 256 * i) * 4, t = f / S, col = f % S;
+    store4(Ks + t * kKP + col, kv[i]);
   }
   // cumulative log-decay (inclusive prefix sum across wave 0) and beta
   if (wv == 0) {
-    const int t = t0 + lane;
-    const bool ok = t < n_tokens;
-    const int64_t gi = (n * n_tokens + t) * n_v_heads + h;
-    double gc = ok ? (double)g[gi] : 0.0;
+    const bool ok = t0 + lane < n_tokens;
+    double gc = ok ? (double)g_raw : 0.0;
 #pragma unroll
     for (int off = 1; off < C; off <<= 1) {
       const double up = __shfl_up(gc, off);
       gc = lane >= off ? gc + up : gc;
     }
     Gs[lane] = gc;
-    Bs[lane] = ok ? beta[gi] : 0.0f;
+    Bs[lane] = ok ? b_raw : 0.0f;
   }
   __syncthreads();
   if (tid < C) {
