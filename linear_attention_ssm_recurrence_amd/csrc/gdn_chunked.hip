@@ -16,15 +16,17 @@
 // (U, V, Y are C x Dv with rows per position; Q, K are C x Dk.)
 //
 // Two kernels:
-//  chunk_prep_kernel  one block per (sequence, V-head, chunk), all chunks in
-//                     parallel: Gc (summed in fp64: under strong decay it
-//                     reaches thousands, where an fp32 difference Gc_t - Gc_s
-//                     would lose ~1e-4), K K^T and Q K^T (lower tiles, MFMA),
-//                     A and P, X blockwise (16 x 16 diagonal tiles by forward
+//  chunk_prep_kernel  one block per (sequence, K-head, chunk), all chunks in
+//                     parallel: K K^T and Q K^T (lower tiles, MFMA) once per
+//                     K-head, then for each V-head that reads it: Gc (summed
+//                     in fp64: under strong decay it reaches thousands, where
+//                     an fp32 difference Gc_t - Gc_s would lose ~1e-4), A and
+//                     P, X blockwise (16 x 16 diagonal tiles by forward
 //                     substitution, the others by MFMA). Writes gamma,
-//                     gamma_C/gamma, beta, X and P to the workspace. Q is read
-//                     as register fragments and K's LDS region is reused for
-//                     A and X, so a block needs ~39 KB (four per CU).
+//                     gamma_C/gamma, beta, X and P of every V-head to the
+//                     workspace. Q is read as register fragments and K's LDS
+//                     region is reused for A and X, so a block needs ~39 KB
+//                     (four per CU).
 //  chunk_scan_kernel  one block per (sequence, V-head, 16 state rows), the
 //                     chunks in order: the 16 rows stay on chip, and per chunk
 //                     each of the 4 waves does 128 MFMAs (K M^T and Q M^T,
@@ -112,18 +114,21 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
   float* Xs = Sm + C * kAP;       // [C][kAP]
   float* Ts = Sm + 2 * C * kAP;   // [3][16][kTP]
 
+  // One block per (sequence, K-head, chunk). K K^T and Q K^T depend only on
+  // the K-head, so they are computed once and kept in registers; A, P and X,
+  // which take each V-head's gate and beta, are then formed for the V-heads
+  // kh, kh + HK, ... (V-head h reads K-head h mod HK) one after the other.
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int64_t unit = blockIdx.x;                    // (n * H + h) * n_chunks + c
-  const int chunk = (int)(unit % n_chunks);
-  const int64_t head = unit / n_chunks;               // n * H + h
-  const int64_t n = head / n_v_heads;
-  const int h = (int)(head % n_v_heads);
-  const int kh = h % n_k_heads;
+  const int64_t kunit = blockIdx.x;                   // (n * HK + kh) * n_chunks + c
+  const int chunk = (int)(kunit % n_chunks);
+  const int64_t khead = kunit / n_chunks;             // n * HK + kh
+  const int64_t n = khead / n_k_heads;
+  const int kh = (int)(khead % n_k_heads);
+  const int gq = n_v_heads / n_k_heads;
   const int t0 = chunk * C;
   const int64_t kq_tok = (int64_t)n_k_heads * S;
   const float* kn = k + (n * n_tokens) * kq_tok + (int64_t)kh * S;
   const float* qn = q + (n * n_tokens) * kq_tok + (int64_t)kh * S;
-  ChunkUnit u = chunk_unit(ws, unit);
 
   // Gram tiles (lower tiles only, ti >= tj): the Q-waves (0, 1) compute
   // Q K^T, the K-waves (2, 3) K K^T, each on the tiles of two tile rows,
@@ -167,38 +172,39 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     const int tt = t0 + t < n_tokens ? t0 + t : n_tokens - 1;
     kv[i] = load4(kn + (int64_t)tt * kq_tok + col);
   }
-  // g and beta of the chunk (wave 0), issued after K: outstanding loads
-  // complete in issue order, so K's stores below do not wait for them
+  // g and beta of one V-head over the chunk (wave 0), issued after K:
+  // outstanding loads complete in issue order, so K's stores below do not
+  // wait for them
+  const bool valid = t0 + lane < n_tokens;
+  const int64_t g_row = (n * n_tokens + (valid ? t0 + lane : n_tokens - 1)) * n_v_heads;
   float g_raw = 0.0f, b_raw = 0.0f;
-  if (wv == 0) {
-    const int t = t0 + lane < n_tokens ? t0 + lane : n_tokens - 1;
-    const int64_t gi = (n * n_tokens + t) * n_v_heads + h;
-    g_raw = g[gi];
-    b_raw = beta[gi];
-  }
+  auto load_gate = [&](int h) {
+    if (wv == 0) {
+      g_raw = g[g_row + h];
+      b_raw = beta[g_row + h];
+    }
+  };
+  // cumulative log-decay (inclusive prefix sum across wave 0) and beta
+  auto prefix = [&]() {
+    if (wv == 0) {
+      double gc = valid ? (double)g_raw : 0.0;
+#pragma unroll
+      for (int off = 1; off < C; off <<= 1) {
+        const double up = __shfl_up(gc, off);
+        gc = lane >= off ? gc + up : gc;
+      }
+      Gs[lane] = gc;
+      Bs[lane] = valid ? b_raw : 0.0f;
+    }
+  };
+  load_gate(kh);
 #pragma unroll
   for (int i = 0; i < KF; ++i) {
     const int f = (tid + 256 * i) * 4, t = f / S, col = f % S;
     store4(Ks + t * kKP + col, kv[i]);
   }
-  // cumulative log-decay (inclusive prefix sum across wave 0) and beta
-  if (wv == 0) {
-    const bool ok = t0 + lane < n_tokens;
-    double gc = ok ? (double)g_raw : 0.0;
-#pragma unroll
-    for (int off = 1; off < C; off <<= 1) {
-      const double up = __shfl_up(gc, off);
-      gc = lane >= off ? gc + up : gc;
-    }
-    Gs[lane] = gc;
-    Bs[lane] = ok ? b_raw : 0.0f;
-  }
+  prefix();
   __syncthreads();
-  if (tid < C) {
-    u.gam[tid] = expf((float)Gs[tid]);
-    u.ktf[tid] = expf((float)(Gs[C - 1] - Gs[tid]));
-    u.bet[tid] = Bs[tid];
-  }
 
   f32x4v acc5[5];
 #pragma unroll
@@ -233,88 +239,113 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     acc5[m] = acc;
   }
   __syncthreads();   // K no longer needed: A and X overwrite it
-#pragma unroll
-  for (int m = 0; m < 5; ++m) {
-    int ti, tj;
-    tile_at(m, ti, tj);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = ti * 16 + g4 * 4 + i, s = tj * 16 + l16;
-      const float r = expf((float)(Gs[t] - Gs[s]));
-      if (qwave) {
-        u.p[frag_index(t, s, 4)] = (s <= t) ? r * acc5[m][i] : 0.0f;
-      } else {
-        As[t * kAP + s] = (s < t) ? Bs[t] * r * acc5[m][i] : 0.0f;
-      }
-    }
-  }
-  // upper tiles: A is not read there; P is stored as zero (whole tiles)
-  for (int f = tid; f < 16 * 256; f += 256) {
-    const int tile = f >> 8, ti = tile >> 2, tj = tile & 3;
-    if (tj > ti) u.p[f] = 0.0f;
-  }
-  __syncthreads();
 
-  // X = (I + A)^-1 blockwise on 16 x 16 tiles. Diagonal tiles: wave w
-  // inverts tile (w, w) by forward substitution, one column per lane (the
-  // four 16-lane groups compute the same columns; group 0 stores them).
-  {
-    const int b = wv, col = l16;
-    float xr[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const float* arow = As + (16 * b + t) * kAP + 16 * b;
-      float acc = 0.0f;
-#pragma unroll
-      for (int s2 = 0; s2 < t; ++s2) acc = __builtin_fmaf(arow[s2], xr[s2], acc);
-      xr[t] = (t == col ? 1.0f : 0.0f) - acc;
+  for (int r = 0; r < gq; ++r) {
+    // The lane indices of the body come from a copy the compiler cannot see
+    // through, so its address arithmetic is redone per V-head instead of
+    // being hoisted out of the loop, where it would hold some fifty
+    // registers through every iteration.
+    int tid_r = tid;
+    asm volatile("" : "+v"(tid_r));
+    const int g4r = (tid_r & 63) >> 4, l16r = tid_r & 15;
+    const int h = kh + r * n_k_heads;
+    const ChunkUnit u = chunk_unit(ws, ((n * n_v_heads + h) * n_chunks + chunk));
+    if (r + 1 < gq) load_gate(h + n_k_heads);   // lands during this V-head's work
+    if (tid_r < C) {
+      u.gam[tid_r] = expf((float)Gs[tid_r]);
+      u.ktf[tid_r] = expf((float)(Gs[C - 1] - Gs[tid_r]));
+      u.bet[tid_r] = Bs[tid_r];
     }
-    if (g4 == 0) {
 #pragma unroll
-      for (int t = 0; t < 16; ++t) Xs[(16 * b + t) * kAP + 16 * b + col] = xr[t];
-    }
-    for (int f = tid; f < C * C; f += 256) {   // X is lower block-triangular
-      const int t = f / C, s2 = f % C;
-      if ((s2 >> 4) > (t >> 4)) Xs[t * kAP + s2] = 0.0f;
-    }
-  }
-  __syncthreads();
-  // Off-diagonal tiles, one block row at a time:
-  //   X_ij = -X_ii (sum_{j <= m < i} A_im X_mj),   wave j computes tile (i, j)
-  for (int bi = 1; bi < 4; ++bi) {
-    const int bj = wv;
-    if (bj < bi) {
-      f32x4v acc = {0.f, 0.f, 0.f, 0.f};
-      for (int bm = bj; bm < bi; ++bm) {
-        const float4 a4 = load4(As + (16 * bi + l16) * kAP + 16 * bm + 4 * g4);
-        const float* xb = Xs + (16 * bm + 4 * g4) * kAP + 16 * bj + l16;
-        acc = mfma4(a4.x, xb[0 * kAP], acc);
-        acc = mfma4(a4.y, xb[1 * kAP], acc);
-        acc = mfma4(a4.z, xb[2 * kAP], acc);
-        acc = mfma4(a4.w, xb[3 * kAP], acc);
+    for (int m = 0; m < 5; ++m) {
+      int ti, tj;
+      tile_at(m, ti, tj);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = ti * 16 + g4r * 4 + i, s = tj * 16 + l16r;
+        const float rr = expf((float)(Gs[t] - Gs[s]));
+        if (qwave) {
+          u.p[frag_index(t, s, 4)] = (s <= t) ? rr * acc5[m][i] : 0.0f;
+        } else {
+          As[t * kAP + s] = (s < t) ? Bs[t] * rr * acc5[m][i] : 0.0f;
+        }
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Ts[(bj * 16 + 4 * g4 + i) * kTP + l16] = acc[i];
+    }
+    // upper tiles: A is not read there; P is stored as zero (whole tiles)
+    for (int f = tid_r; f < 16 * 256; f += 256) {
+      const int tile = f >> 8, ti = tile >> 2, tj = tile & 3;
+      if (tj > ti) u.p[f] = 0.0f;
     }
     __syncthreads();
-    if (bj < bi) {
-      const float4 x4 = load4(Xs + (16 * bi + l16) * kAP + 16 * bi + 4 * g4);
-      const float* tb = Ts + (bj * 16 + 4 * g4) * kTP + l16;
-      f32x4v acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma4(x4.x, tb[0 * kTP], acc);
-      acc = mfma4(x4.y, tb[1 * kTP], acc);
-      acc = mfma4(x4.z, tb[2 * kTP], acc);
-      acc = mfma4(x4.w, tb[3 * kTP], acc);
+
+    // X = (I + A)^-1 blockwise on 16 x 16 tiles. Diagonal tiles: wave w
+    // inverts tile (w, w) by forward substitution, one column per lane (the
+    // four 16-lane groups compute the same columns; group 0 stores them).
+    {
+      const int b = wv, col = l16r;
+      float xr[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Xs[(16 * bi + 4 * g4 + i) * kAP + 16 * bj + l16] = -acc[i];
+      for (int t = 0; t < 16; ++t) {
+        const float* arow = As + (16 * b + t) * kAP + 16 * b;
+        float acc = 0.0f;
+#pragma unroll
+        for (int s2 = 0; s2 < t; ++s2) acc = __builtin_fmaf(arow[s2], xr[s2], acc);
+        xr[t] = (t == col ? 1.0f : 0.0f) - acc;
+      }
+      if (g4r == 0) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) Xs[(16 * b + t) * kAP + 16 * b + col] = xr[t];
+      }
+      for (int f = tid_r; f < C * C; f += 256) {   // X is lower block-triangular
+        const int t = f / C, s2 = f % C;
+        if ((s2 >> 4) > (t >> 4)) Xs[t * kAP + s2] = 0.0f;
+      }
     }
     __syncthreads();
-  }
-  // X, written in fragment order (one float4 per thread and step)
-  for (int f4 = tid; f4 < C * C / 4; f4 += 256) {
-    const int tile = f4 >> 6, ln = f4 & 63;
-    const int t = (tile >> 2) * 16 + (ln & 15), s0 = (tile & 3) * 16 + (ln >> 4) * 4;
-    store4(u.x + 4 * f4, load4(Xs + t * kAP + s0));
+    // Off-diagonal tiles, one block row at a time:
+    //   X_ij = -X_ii (sum_{j <= m < i} A_im X_mj),   wave j computes tile (i, j)
+    for (int bi = 1; bi < 4; ++bi) {
+      const int bj = wv;
+      if (bj < bi) {
+        f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+        for (int bm = bj; bm < bi; ++bm) {
+          const float4 a4 = load4(As + (16 * bi + l16r) * kAP + 16 * bm + 4 * g4r);
+          const float* xb = Xs + (16 * bm + 4 * g4r) * kAP + 16 * bj + l16r;
+          acc = mfma4(a4.x, xb[0 * kAP], acc);
+          acc = mfma4(a4.y, xb[1 * kAP], acc);
+          acc = mfma4(a4.z, xb[2 * kAP], acc);
+          acc = mfma4(a4.w, xb[3 * kAP], acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Ts[(bj * 16 + 4 * g4r + i) * kTP + l16r] = acc[i];
+      }
+      __syncthreads();
+      if (bj < bi) {
+        const float4 x4 = load4(Xs + (16 * bi + l16r) * kAP + 16 * bi + 4 * g4r);
+        const float* tb = Ts + (bj * 16 + 4 * g4r) * kTP + l16r;
+        f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma4(x4.x, tb[0 * kTP], acc);
+        acc = mfma4(x4.y, tb[1 * kTP], acc);
+        acc = mfma4(x4.z, tb[2 * kTP], acc);
+        acc = mfma4(x4.w, tb[3 * kTP], acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Xs[(16 * bi + 4 * g4r + i) * kAP + 16 * bj + l16r] = -acc[i];
+      }
+      __syncthreads();
+    }
+    // X, written in fragment order (one float4 per thread and step)
+    for (int f4 = tid_r; f4 < C * C / 4; f4 += 256) {
+      const int tile = f4 >> 6, ln = f4 & 63;
+      const int t = (tile >> 2) * 16 + (ln & 15), s0 = (tile & 3) * 16 + (ln >> 4) * 4;
+      store4(u.x + 4 * f4, load4(Xs + t * kAP + s0));
+    }
+    // the next V-head's prefix sum; Gs and Bs were last read before the
+    // barriers above, and the barrier below orders the X write-out before
+    // the next iteration overwrites As and Xs
+    if (r + 1 < gq) {
+      prefix();
+      __syncthreads();
+    }
   }
 }
 
@@ -593,11 +624,12 @@ extern "C" int gdn_recurrence_seq_chunked(float* state, const float* q, const fl
     return GDN_EALIGN;
   const int n_chunks = (n_tokens + kChC - 1) / kChC;
   const int64_t units = (int64_t)n_seqs * n_v_heads * n_chunks;
+  const int64_t prep_blocks = (int64_t)n_seqs * n_k_heads * n_chunks;   // one per K-head and chunk
   const int64_t scan_blocks = (int64_t)n_seqs * n_v_heads * (kChS / kChR);
   if (units >= (int64_t(1) << 31) || scan_blocks >= (int64_t(1) << 31)) return GDN_ESIZE;
   hipStream_t s = as_stream(stream);
   float* ws = reinterpret_cast<float*>(workspace);
-  hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)units), dim3(256), 0, s, q, k, g, beta, ws,
+  hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)prep_blocks), dim3(256), 0, s, q, k, g, beta, ws,
                      n_tokens, n_k_heads, n_v_heads, n_chunks);
   int rc = launch_status();
   if (rc != GDN_OK) return rc;
