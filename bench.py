@@ -271,8 +271,8 @@ def run_scan(torch, gdn, inputs, steps, warmup):
         "scan_algorithmic_bytes": scan_bytes,
         "chunked_scan_ms": t_chunk.event_ms / steps,
         "chunked_scan_tokens_per_s": N * T / (t_chunk.event_ms / steps * 1e-3),
-        "chunked_mfma_TFLOPs": chunked_mfma_flops(N, T, H) / (t_chunk.event_ms / steps * 1e-3) / 1e12,
-        "chunked_frac_fp32_mfma_peak": chunked_mfma_flops(N, T, H) / (t_chunk.event_ms / steps * 1e-3)
+        "chunked_mfma_TFLOPs": chunked_mfma_flops(N, T, H, q.shape[2]) / (t_chunk.event_ms / steps * 1e-3) / 1e12,
+        "chunked_frac_fp32_mfma_peak": chunked_mfma_flops(N, T, H, q.shape[2]) / (t_chunk.event_ms / steps * 1e-3)
                                        / 1e12 / FP32_MFMA_PEAK_TFLOPS,
         "conv_kernel_ms": conv_ms,
         "conv_GBps": conv_bytes / (conv_ms * 1e-3) / 1e9,
@@ -285,14 +285,14 @@ def w_scan_tokens(leg) -> float:
     return leg["tokens_per_s"] * leg["ms_per_step"] * 1e-3
 
 
-def chunked_mfma_flops(N, T, H) -> float:
+def chunked_mfma_flops(N, T, H, HK=None) -> float:
     """fp32 MFMA work of one chunked scan at S = 128 (v_mfma_f32_16x16x4f32,
-    2048 flop each): per 64-position chunk and head, the preparation runs 704
-    (20 Gram tiles x 32, 64 for the blockwise inverse) and the scan's 8 row
-    blocks x 4 waves run 128 each."""
+    2048 flop each): per 64-position chunk, the preparation runs 640 per
+    K-head (20 Gram tiles x 32) and 64 per V-head (the blockwise inverse),
+    and the scan's 8 row blocks x 4 waves run 128 each per V-head."""
+    HK = H if HK is None else HK
     chunks = (T + 63) // 64
-    per_head_chunk = 704 + 8 * 4 * 128
-    return 2048.0 * N * H * chunks * per_head_chunk
+    return 2048.0 * N * chunks * (HK * 640 + H * (64 + 8 * 4 * 128))
 
 
 def run_spec(torch, gdn, inputs, steps, warmup):
