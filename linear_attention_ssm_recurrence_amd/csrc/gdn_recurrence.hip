@@ -135,7 +135,7 @@ static int launch_short_scan(float* state, const float* q, const float* k, const
 // ---------------------------------------------------------------------------
 // Scan: a block of W waves owns R = W*G consecutive rows of one (sequence,
 // head) and carries them in VGPRs through all tokens. Per chunk of CT tokens
-// (64; 16 at S = 256, where LDS is the limit)
+// (64 or 32, chosen by the grid below; 16 at S = 256, where LDS is the limit)
 // the block stages k and q of its head, v of its rows, and exp(g) and beta
 // into LDS; the next chunk's global loads are issued before the current chunk
 // is computed and land in the other LDS buffer, so there is one barrier per
