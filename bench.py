@@ -621,7 +621,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: the gated delta-rule path shards by sequence and "
-              "head with no exchange, and this build measures one GPU's share (use --gpus 1).",
+              "head with no exchange, and the benchmark measures one GPU's share (use --gpus 1).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -50,7 +50,7 @@ extern "C" {
 #define GDN_OK 0
 #define GDN_ENULL 1        /* a required pointer is NULL */
 #define GDN_ESIZE 2        /* a shape <= 0, a count < 0, too large, or sizes disagree */
-#define GDN_EUNSUPPORTED 3 /* a shape this build has no kernel for */
+#define GDN_EUNSUPPORTED 3 /* a shape the library has no kernel for */
 #define GDN_EALIGN 4       /* a float4-accessed pointer is not 16-byte aligned */
 #define GDN_ELAUNCH 5      /* the HIP runtime rejected a kernel launch */
 

@@ -6,7 +6,7 @@ extern "C" const char* gdn_strerror(int code) {
     case GDN_OK: return "success";
     case GDN_ENULL: return "a required pointer is NULL";
     case GDN_ESIZE: return "a size is non-positive, too large, or inconsistent with another";
-    case GDN_EUNSUPPORTED: return "shape not supported by this build";
+    case GDN_EUNSUPPORTED: return "shape not supported by the library";
     case GDN_EALIGN: return "a float4-accessed pointer is not 16-byte aligned";
     case GDN_ELAUNCH: return "the HIP runtime rejected a kernel launch";
   }
