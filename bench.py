@@ -227,6 +227,9 @@ def run_scan(torch, gdn, inputs, steps, warmup):
     def scan():
         gdn.gdn_recurrence_seq(st, q, k, v, g, beta, y, w.scale)
 
+    def scan_t4():   # the same scan with the "T4" read-out (same state, y regrouped)
+        gdn.gdn_recurrence_seq_ex(st, q, k, v, g, beta, y, w.scale, variant=gdn.GDN_RECUR_T4)
+
     ws = torch.empty(gdn.gdn_chunked_workspace_bytes(N, T, H, S), dtype=torch.uint8, device="cuda")
 
     def chunked():
@@ -252,6 +255,10 @@ def run_scan(torch, gdn, inputs, steps, warmup):
     with Timer(torch) as t_chunk:
         for _ in range(steps):
             chunked()
+    scan_t4()
+    with Timer(torch) as t_t4:
+        for _ in range(steps):
+            scan_t4()
     ms = t_all.wall_ms / steps
     scan_ms = t_scan.event_ms / steps
     conv_ms = t_conv.event_ms / steps
@@ -269,6 +276,7 @@ def run_scan(torch, gdn, inputs, steps, warmup):
         "scan_TFLOPs": flops / (scan_ms * 1e-3) / 1e12,
         "scan_frac_fp32_vector_peak": flops / (scan_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
         "scan_algorithmic_bytes": scan_bytes,
+        "scan_t4_kernel_ms": t_t4.event_ms / steps,
         "chunked_scan_ms": t_chunk.event_ms / steps,
         "chunked_scan_tokens_per_s": N * T / (t_chunk.event_ms / steps * 1e-3),
         "chunked_mfma_TFLOPs": chunked_mfma_flops(N, T, H, q.shape[2]) / (t_chunk.event_ms / steps * 1e-3) / 1e12,

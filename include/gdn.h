@@ -176,17 +176,22 @@ int gdn_recurrence_ex(float *state, const float *q, const float *k, const float 
 
 /*
  * gdn_recurrence_seq with the grouped-query repeat done by index (q, k are
- * [n_seqs][n_tokens][n_k_heads][S]) and optional per-token snapshots for
- * speculative decoding ([CU] fc_ssm_recurrence_seq, "snaps"): when snaps is
- * not NULL, snaps[n][t] (n_v_heads*S*S floats, the state layout) receives the
- * state after token t of sequence n, so a caller that accepts the first M
- * tokens restores snaps[n][M-1]. snaps [n_seqs][n_tokens][n_v_heads][S][S],
- * 16-byte aligned, caller-owned. Errors as gdn_recurrence_seq.
+ * [n_seqs][n_tokens][n_k_heads][S]), optional per-token snapshots for
+ * speculative decoding ([CU] fc_ssm_recurrence_seq, "snaps"), and the read-out
+ * variant of gdn_recurrence_ex ([CU] "T4", fc_ssm_recurrence_slots_2pass,
+ * applied per token). When snaps is not NULL, snaps[n][t] (n_v_heads*S*S
+ * floats, the state layout) receives the state after token t of sequence n,
+ * so a caller that accepts the first M tokens restores snaps[n][M-1]. snaps
+ * [n_seqs][n_tokens][n_v_heads][S][S], 16-byte aligned, caller-owned.
+ * variant: GDN_RECUR_EXACT, or GDN_RECUR_T4 (the state, and the snapshots, are
+ * those of the exact variant bit for bit; y is reassociated and equals
+ * gdn_recurrence_ex with GDN_RECUR_T4 applied token by token, bit for bit).
+ * Errors as gdn_recurrence_seq, plus GDN_EUNSUPPORTED for an unknown variant.
  */
 int gdn_recurrence_seq_ex(float *state, const float *q, const float *k, const float *v,
                           const float *g, const float *beta, float *y, float *snaps, int n_seqs,
                           int n_tokens, int n_k_heads, int n_v_heads, int state_size, float scale,
-                          void *stream);
+                          int variant, void *stream);
 
 /*
  * gdn_conv1d_silu_seq with optional per-position history snapshots ([CU]

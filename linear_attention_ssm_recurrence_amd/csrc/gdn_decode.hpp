@@ -24,7 +24,8 @@ namespace gdn {
 constexpr int kDecodeWaves = 8;
 
 // With T4 the read-out is regrouped as y = scale * (r_dec . q + delta * qk)
-// (delta_rule_step_t4); qk = k . q is reduced once per wave. The state is the
+// (delta_rule_step_t4); qk = k . q is reduced once per wave, in qk_dot's
+// order, which the scan's T4 form shares. The state is the
 // same either way. V-head h of sequence n reads K-head h mod n_k_heads of q
 // and k (the tiled grouped-query repeat), so q and k are [N][HK][S].
 template <int S, int RW, bool T4>
@@ -52,7 +53,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void recurrence_decode_kernel(
   const float d = expf(g[pair]);
   const float b = beta[pair];
   float qk = 0.0f;
-  if constexpr (T4) qk = group_sum<L>(lane_dot<E>(kk, qq));
+  if constexpr (T4) {   // k . q in qk_dot's order: lane i of each group of S/4 takes entries 4i..4i+3
+    const int i4 = 4 * (lane % (S / 4));
+    qk = qk_dot<S>(load4(k + kq * S + i4), load4(q + kq * S + i4));
+  }
 
   float* sp = state + pair * (int64_t)S * S;
   float4 raw[IT][E / 4];

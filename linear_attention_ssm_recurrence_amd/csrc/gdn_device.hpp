@@ -143,6 +143,21 @@ __device__ __forceinline__ float delta_rule_step(float (&r)[E], const float (&k)
   return scale * o;
 }
 
+// k . q of one head and token for the "T4" read-out, in one fixed order that
+// every kernel using it shares: each lane of an aligned group of S/4 lanes
+// holds the four consecutive entries 4i .. 4i+3 (i its index in the group),
+// forms a four-term chain, and the group sums the chains. Every lane of the
+// group returns the same bits.
+template <int S>
+__device__ __forceinline__ float qk_dot(float4 k, float4 q) {
+  static_assert(S % 4 == 0 && S / 4 <= 64, "a head must fit one group of lanes");
+  float p = k.x * q.x;
+  p = __builtin_fmaf(k.y, q.y, p);
+  p = __builtin_fmaf(k.z, q.z, p);
+  p = __builtin_fmaf(k.w, q.w, p);
+  return group_sum<S / 4>(p);
+}
+
 // The same token with the read-out regrouped as in the "T4" kernel of
 // ssm_gated_delta.cu (fc_ssm_recurrence_slots_2pass): after the decay,
 //   y = scale * (r_dec . q + delta * (k . q)),

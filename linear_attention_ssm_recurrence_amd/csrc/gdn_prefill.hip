@@ -289,7 +289,8 @@ extern "C" int gdn_prefill_bf16_ex(const uint16_t* qkv, const uint16_t* z, const
                                     state_size, scale, stream);
   else
     rc = gdn_recurrence_seq_ex(state, ws.q, ws.k, ws.v, ws.g, ws.beta, ws.y, nullptr, n_seqs,
-                               n_tokens, n_k_heads, n_v_heads, state_size, scale, stream);
+                               n_tokens, n_k_heads, n_v_heads, state_size, scale,
+                               GDN_RECUR_EXACT, stream);
   if (rc != GDN_OK) return rc;
   return launch_gated_rmsnorm_bf16z(ws.y, norm_w, z, out, rows, state_size, eps, s);
 }

@@ -32,7 +32,7 @@ namespace gdn {
 // ---------------------------------------------------------------------------
 constexpr int kShortScan = 16;
 
-template <int S, int RW, bool SNAP>
+template <int S, int RW, bool SNAP, bool T4>
 __global__ __launch_bounds__(64 * kDecodeWaves) void recurrence_short_scan_kernel(
     float* __restrict__ state, const float* __restrict__ q, const float* __restrict__ k,
     const float* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
@@ -73,9 +73,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void recurrence_short_scan_kerne
   }
 
   float kk[E], qq[E], vv[IT], gg, bb;
+  float4 k4 = make_float4(0.f, 0.f, 0.f, 0.f), q4 = k4;   // T4: k, q in qk_dot's layout
+  const int i4 = 4 * (lane % (S / 4));
   auto read = [&](int t) {
     load_row_part<E, L>(kn + t * tok_k, p, kk);
     load_row_part<E, L>(qn + t * tok_k, p, qq);
+    if constexpr (T4) {
+      k4 = load4(kn + t * tok_k + i4);
+      q4 = load4(qn + t * tok_k + i4);
+    }
 #pragma unroll
     for (int it = 0; it < IT; ++it) vv[it] = vn[t * tok_v + it * G];
     gg = gn[(int64_t)t * n_v_heads];
@@ -93,10 +99,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void recurrence_short_scan_kerne
     for (int it = 0; it < IT; ++it) vc[it] = vv[it];
     const float d = expf(gg);
     const float b = bb;
+    float qk = 0.0f;
+    if constexpr (T4) qk = qk_dot<S>(k4, q4);
     if (t + 1 < n_tokens) read(t + 1);
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const float yj = delta_rule_step<E, L>(r[it], kc, qc, vc[it], d, b, scale);
+      const float yj = T4 ? delta_rule_step_t4<E, L>(r[it], kc, qc, vc[it], d, b, qk, scale)
+                          : delta_rule_step<E, L>(r[it], kc, qc, vc[it], d, b, scale);
       if (p == 0) yn[t * tok_v + it * G] = yj;
       if constexpr (SNAP) {
         // snapshots: ordinary stores (measured 6% faster here than streaming
@@ -118,7 +127,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void recurrence_short_scan_kerne
                     make_float4(r[it][4 * m], r[it][4 * m + 1], r[it][4 * m + 2], r[it][4 * m + 3]));
 }
 
-template <int S, bool SNAP>
+template <int S, bool SNAP, bool T4>
 static int launch_short_scan(float* state, const float* q, const float* k, const float* v,
                              const float* g, const float* beta, float* y, float* snaps, int n_seqs,
                              int n_tokens, int n_k_heads, int n_v_heads, float scale,
@@ -126,7 +135,7 @@ static int launch_short_scan(float* state, const float* q, const float* k, const
   constexpr int RW = DecodeCfg<S>::RW;
   const int64_t n_pairs = (int64_t)n_seqs * n_v_heads;
   const unsigned blocks = grid_for(n_pairs * (S / RW), kDecodeWaves);
-  hipLaunchKernelGGL((recurrence_short_scan_kernel<S, RW, SNAP>), dim3(blocks),
+  hipLaunchKernelGGL((recurrence_short_scan_kernel<S, RW, SNAP, T4>), dim3(blocks),
                      dim3(64 * kDecodeWaves), 0, stream, state, q, k, v, g, beta, y, snaps, n_pairs,
                      n_tokens, n_k_heads, n_v_heads, scale);
   return launch_status();
@@ -167,12 +176,13 @@ struct ScanCfg {
   static constexpr int BPH = S / R;                               // blocks per head
   static constexpr int CT = S >= 256 ? 16 : (LONG_CHUNK ? 64 : 32);  // tokens per chunk
   static constexpr int THREADS = 64 * W;
-  // LDS words of one chunk buffer: k, q [CT][S], v [CT][R], decay, beta [CT]
+  // LDS words of one chunk buffer: k, q [CT][S], v [CT][R], decay, beta, k . q [CT]
   static constexpr int KQ = CT * S;
   static constexpr int VOFF = 2 * KQ;
   static constexpr int DOFF = VOFF + CT * R;
   static constexpr int BOFF = DOFF + CT;
-  static constexpr int BUF = BOFF + CT;
+  static constexpr int QOFF = BOFF + CT;   // k . q per token (the T4 read-out)
+  static constexpr int BUF = QOFF + CT;
   // float4 loads of k and q per thread per chunk (each of k and q)
   static constexpr int KQ4 = KQ / 4 / THREADS;
   static constexpr int VPT = (CT * R + THREADS - 1) / THREADS;    // v loads per thread
@@ -180,7 +190,7 @@ struct ScanCfg {
   static_assert(CT <= THREADS, "one staging thread per token");
 };
 
-template <int S, bool LONG_CHUNK, bool SNAP>
+template <int S, bool LONG_CHUNK, bool SNAP, bool T4>
 __global__ __launch_bounds__((ScanCfg<S, LONG_CHUNK>::THREADS)) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void recurrence_scan_kernel(
     float* __restrict__ state, const float* __restrict__ q, const float* __restrict__ k,
@@ -217,8 +227,12 @@ void recurrence_scan_kernel(
   const float* gn = g + base_n * n_v_heads + h;
   const float* bn = beta + base_n * n_v_heads + h;
 
-  // Registers that carry one chunk from global memory to LDS.
+  // Registers that carry one chunk from global memory to LDS (zeroed so that
+  // the T4 sums of positions past the end read defined values; those sums
+  // are not stored).
   float4 pk[Cfg::KQ4], pq[Cfg::KQ4];
+#pragma unroll
+  for (int i = 0; i < Cfg::KQ4; ++i) pk[i] = pq[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   float pv[Cfg::VPT];
   float pdec = 0.0f, pbeta = 0.0f;
 
@@ -263,6 +277,17 @@ void recurrence_scan_kernel(
       buf[Cfg::DOFF + tid] = pdec;
       buf[Cfg::BOFF + tid] = pbeta;
     }
+    // T4: k . q of each token. The S/4 consecutive threads that hold a
+    // token's k and q pieces form an aligned group with entries 4i..4i+3 in
+    // its thread i: qk_dot's layout, so the value equals the decode's.
+    if constexpr (T4) {
+#pragma unroll
+      for (int i = 0; i < Cfg::KQ4; ++i) {
+        const int f = (i * THREADS + tid) * 4;
+        const float qk = qk_dot<S>(pk[i], pq[i]);
+        if (f % S == 0 && f / S < ct) buf[Cfg::QOFF + f / S] = qk;
+      }
+    }
   };
 
   float r[E];
@@ -290,25 +315,29 @@ void recurrence_scan_kernel(
     const float vj = buf[Cfg::VOFF + tt * R + lrow];
     const float d = buf[Cfg::DOFF + tt];
     const float b = buf[Cfg::BOFF + tt];
-    ysm[tt * R + lrow] = delta_rule_step<E, L>(r, kk, qq, vj, d, b, scale);
+    ysm[tt * R + lrow] = T4 ? delta_rule_step_t4<E, L>(r, kk, qq, vj, d, b, buf[Cfg::QOFF + tt], scale)
+                            : delta_rule_step<E, L>(r, kk, qq, vj, d, b, scale);
   };
   // A full chunk with the next token's LDS reads issued before the current
   // token's arithmetic (two register sets, rotated by the unrolled loop).
   auto full_chunk = [&](const float* buf, int t0) {
-    float kk[2][E], qq[2][E], vj[2], d[2], b[2];
+    float kk[2][E], qq[2][E], vj[2], d[2], b[2], qk[2];
     auto read = [&](int tt, int slot) {
       load_row_part<E, L>(buf + tt * S, p, kk[slot]);
       load_row_part<E, L>(buf + KQ + tt * S, p, qq[slot]);
       vj[slot] = buf[Cfg::VOFF + tt * R + lrow];
       d[slot] = buf[Cfg::DOFF + tt];
       b[slot] = buf[Cfg::BOFF + tt];
+      qk[slot] = T4 ? buf[Cfg::QOFF + tt] : 0.0f;
     };
     read(0, 0);
 #pragma unroll
     for (int tt = 0; tt < CT; ++tt) {
       const int cur = tt & 1;
       if (tt + 1 < CT) read(tt + 1, cur ^ 1);
-      ysm[tt * R + lrow] = delta_rule_step<E, L>(r, kk[cur], qq[cur], vj[cur], d[cur], b[cur], scale);
+      ysm[tt * R + lrow] =
+          T4 ? delta_rule_step_t4<E, L>(r, kk[cur], qq[cur], vj[cur], d[cur], b[cur], qk[cur], scale)
+             : delta_rule_step<E, L>(r, kk[cur], qq[cur], vj[cur], d[cur], b[cur], scale);
       snapshot(t0 + tt);
     }
   };
@@ -347,23 +376,23 @@ void recurrence_scan_kernel(
     store4(srow + 4 * (p + L * m), make_float4(r[4 * m], r[4 * m + 1], r[4 * m + 2], r[4 * m + 3]));
 }
 
-template <int S, bool SNAP>
+template <int S, bool SNAP, bool T4>
 static int launch_scan(float* state, const float* q, const float* k, const float* v,
                        const float* g, const float* beta, float* y, float* snaps, int n_seqs,
                        int n_tokens, int n_k_heads, int n_v_heads, float scale, hipStream_t stream) {
   if (n_tokens <= kShortScan)
-    return launch_short_scan<S, SNAP>(state, q, k, v, g, beta, y, snaps, n_seqs, n_tokens,
-                                      n_k_heads, n_v_heads, scale, stream);
+    return launch_short_scan<S, SNAP, T4>(state, q, k, v, g, beta, y, snaps, n_seqs, n_tokens,
+                                          n_k_heads, n_v_heads, scale, stream);
   using CfgL = ScanCfg<S, true>;
   using CfgS = ScanCfg<S, false>;
   static_assert(CfgL::BPH == CfgS::BPH && CfgL::THREADS == CfgS::THREADS, "same grid either way");
   const int64_t blocks = (int64_t)n_seqs * n_v_heads * CfgL::BPH;
   if (blocks <= cu_count())
-    hipLaunchKernelGGL((recurrence_scan_kernel<S, true, SNAP>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((recurrence_scan_kernel<S, true, SNAP, T4>), dim3((unsigned)blocks),
                        dim3(CfgL::THREADS), 0, stream, state, q, k, v, g, beta, y, snaps, n_tokens,
                        n_k_heads, n_v_heads, scale);
   else
-    hipLaunchKernelGGL((recurrence_scan_kernel<S, false, SNAP>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((recurrence_scan_kernel<S, false, SNAP, T4>), dim3((unsigned)blocks),
                        dim3(CfgS::THREADS), 0, stream, state, q, k, v, g, beta, y, snaps, n_tokens,
                        n_k_heads, n_v_heads, scale);
   return launch_status();
@@ -401,16 +430,16 @@ static int dispatch_decode(float* state, const float* q, const float* k, const f
   return GDN_EUNSUPPORTED;
 }
 
-template <bool SNAP>
+template <bool SNAP, bool T4>
 static int dispatch_scan(float* state, const float* q, const float* k, const float* v,
                          const float* g, const float* beta, float* y, float* snaps, int n_seqs,
                          int n_tokens, int n_k_heads, int n_v_heads, int state_size, float scale,
                          hipStream_t s) {
   switch (state_size) {
-    case 32: return launch_scan<32, SNAP>(state, q, k, v, g, beta, y, snaps, n_seqs, n_tokens, n_k_heads, n_v_heads, scale, s);
-    case 64: return launch_scan<64, SNAP>(state, q, k, v, g, beta, y, snaps, n_seqs, n_tokens, n_k_heads, n_v_heads, scale, s);
-    case 128: return launch_scan<128, SNAP>(state, q, k, v, g, beta, y, snaps, n_seqs, n_tokens, n_k_heads, n_v_heads, scale, s);
-    case 256: return launch_scan<256, SNAP>(state, q, k, v, g, beta, y, snaps, n_seqs, n_tokens, n_k_heads, n_v_heads, scale, s);
+    case 32: return launch_scan<32, SNAP, T4>(state, q, k, v, g, beta, y, snaps, n_seqs, n_tokens, n_k_heads, n_v_heads, scale, s);
+    case 64: return launch_scan<64, SNAP, T4>(state, q, k, v, g, beta, y, snaps, n_seqs, n_tokens, n_k_heads, n_v_heads, scale, s);
+    case 128: return launch_scan<128, SNAP, T4>(state, q, k, v, g, beta, y, snaps, n_seqs, n_tokens, n_k_heads, n_v_heads, scale, s);
+    case 256: return launch_scan<256, SNAP, T4>(state, q, k, v, g, beta, y, snaps, n_seqs, n_tokens, n_k_heads, n_v_heads, scale, s);
   }
   return GDN_EUNSUPPORTED;
 }
@@ -452,14 +481,16 @@ extern "C" int gdn_recurrence_seq(float* state, const float* q, const float* k, 
   const int rc = check_recurrence(state, q, k, v, g, beta, y, n_seqs, n_tokens, n_v_heads,
                                   n_v_heads, state_size);
   if (rc != GDN_OK) return finish_check(rc);
-  return dispatch_scan<false>(state, q, k, v, g, beta, y, nullptr, n_seqs, n_tokens, n_v_heads,
-                              n_v_heads, state_size, scale, as_stream(stream));
+  return dispatch_scan<false, false>(state, q, k, v, g, beta, y, nullptr, n_seqs, n_tokens,
+                                     n_v_heads, n_v_heads, state_size, scale, as_stream(stream));
 }
 
 extern "C" int gdn_recurrence_seq_ex(float* state, const float* q, const float* k,
                                      const float* v, const float* g, const float* beta, float* y,
                                      float* snaps, int n_seqs, int n_tokens, int n_k_heads,
-                                     int n_v_heads, int state_size, float scale, void* stream) {
+                                     int n_v_heads, int state_size, float scale, int variant,
+                                     void* stream) {
+  if (variant != GDN_RECUR_EXACT && variant != GDN_RECUR_T4) return GDN_EUNSUPPORTED;
   const int rc = check_recurrence(state, q, k, v, g, beta, y, n_seqs, n_tokens, n_k_heads,
                                   n_v_heads, state_size);
   if (rc != GDN_OK) return finish_check(rc);
@@ -469,9 +500,14 @@ extern "C" int gdn_recurrence_seq_ex(float* state, const float* q, const float* 
                        &snap_elems))
     return GDN_ESIZE;
   hipStream_t s = as_stream(stream);
+  const bool t4 = variant == GDN_RECUR_T4;
   if (snaps)
-    return dispatch_scan<true>(state, q, k, v, g, beta, y, snaps, n_seqs, n_tokens, n_k_heads,
-                               n_v_heads, state_size, scale, s);
-  return dispatch_scan<false>(state, q, k, v, g, beta, y, nullptr, n_seqs, n_tokens, n_k_heads,
-                              n_v_heads, state_size, scale, s);
+    return t4 ? dispatch_scan<true, true>(state, q, k, v, g, beta, y, snaps, n_seqs, n_tokens,
+                                          n_k_heads, n_v_heads, state_size, scale, s)
+              : dispatch_scan<true, false>(state, q, k, v, g, beta, y, snaps, n_seqs, n_tokens,
+                                           n_k_heads, n_v_heads, state_size, scale, s);
+  return t4 ? dispatch_scan<false, true>(state, q, k, v, g, beta, y, nullptr, n_seqs, n_tokens,
+                                         n_k_heads, n_v_heads, state_size, scale, s)
+            : dispatch_scan<false, false>(state, q, k, v, g, beta, y, nullptr, n_seqs, n_tokens,
+                                          n_k_heads, n_v_heads, state_size, scale, s);
 }

@@ -56,7 +56,7 @@ def load_library():
         "gdn_conv1d_silu_seq": [P, P, P, P, I, I, I, I, P],
         "gdn_recurrence": [P, P, P, P, P, P, P, I, I, I, F, P],
         "gdn_recurrence_ex": [P, P, P, P, P, P, P, I, I, I, I, F, I, P],
-        "gdn_recurrence_seq_ex": [P, P, P, P, P, P, P, P, I, I, I, I, I, F, P],
+        "gdn_recurrence_seq_ex": [P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, P],
         "gdn_conv1d_silu_seq_ex": [P, P, P, P, P, I, I, I, I, P],
         "gdn_recurrence_seq": [P, P, P, P, P, P, P, I, I, I, I, F, P],
         "gdn_gated_rmsnorm": [P, P, P, P, L, I, F, P],
@@ -216,9 +216,11 @@ def gdn_recurrence_ex(state, q, k, v, g, beta, y, scale, variant=GDN_RECUR_EXACT
           N, HK, H, S, float(scale), int(variant), _stream(v, stream))
 
 
-def gdn_recurrence_seq_ex(state, q, k, v, g, beta, y, scale, snaps=None, stream=None):
+def gdn_recurrence_seq_ex(state, q, k, v, g, beta, y, scale, snaps=None,
+                          variant=GDN_RECUR_EXACT, stream=None):
     """state [N][H][S][S] in place; q, k [N][T][HK][S]; v, y [N][T][H][S];
-    g, beta [N][T][H]; snaps None or [N][T][H][S][S] (state after each token)."""
+    g, beta [N][T][H]; snaps None or [N][T][H][S][S] (state after each token);
+    variant GDN_RECUR_EXACT or GDN_RECUR_T4 (the read-out of gdn_recurrence_ex)."""
     N, T, H, S = v.shape
     HK = q.shape[2]
     _shape(state, (N, H, S, S), "state")
@@ -233,7 +235,7 @@ def gdn_recurrence_seq_ex(state, q, k, v, g, beta, y, scale, snaps=None, stream=
         sp = _ptr(snaps, F32, "snaps")
     _call("gdn_recurrence_seq_ex", _ptr(state, F32, "state"), _ptr(q, F32, "q"), _ptr(k, F32, "k"),
           _ptr(v, F32, "v"), _ptr(g, F32, "g"), _ptr(beta, F32, "beta"), _ptr(y, F32, "y"), sp,
-          N, T, HK, H, S, float(scale), _stream(v, stream))
+          N, T, HK, H, S, float(scale), int(variant), _stream(v, stream))
 
 
 def gdn_conv1d_silu_seq_ex(x, w, conv_state, out, snaps=None, stream=None):

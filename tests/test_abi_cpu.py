@@ -129,9 +129,13 @@ def test_ex_validation(lib):
     assert rex(state=NUL, n=0) == gdn.GDN_OK
     fs = lib.gdn_recurrence_seq_ex
 
-    def rsx(snaps=NUL, HK=2, T=3, n=1):
-        return fs(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, snaps, n, T, HK, 4, 32, 1.0, NUL)
+    def rsx(snaps=NUL, HK=2, T=3, n=1, variant=gdn.GDN_RECUR_EXACT):
+        return fs(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, snaps, n, T, HK, 4, 32, 1.0, variant,
+                  NUL)
 
+    assert rsx(variant=2) == gdn.GDN_EUNSUPPORTED
+    assert rsx(variant=-1, n=0) == gdn.GDN_EUNSUPPORTED    # checked before anything else
+    assert rsx(variant=gdn.GDN_RECUR_T4, T=0) == gdn.GDN_OK
     assert rsx(snaps=FAKE_MIS) == gdn.GDN_EALIGN
     assert rsx(HK=3) == gdn.GDN_ESIZE
     assert rsx(T=-1) == gdn.GDN_ESIZE

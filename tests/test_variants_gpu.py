@@ -195,3 +195,50 @@ def test_scan_many_blocks_short_chunks():
                               sl(p["beta"]), y_d, scale, gdn.GDN_RECUR_EXACT)
         assert torch.equal(y[:, t], y_d), f"token {t}: scan y != decode launch y"
     assert torch.equal(st, st_d), "scan state != chained decode launches"
+
+
+def _scan_t4_case(seed, N, T, HK, H, S, with_snaps):
+    """The scan with the "T4" read-out: y against the oracle within the
+    tolerance and against gdn_recurrence_ex(GDN_RECUR_T4) applied token by
+    token bit for bit; the state (and the snapshots) against the exact scan
+    bit for bit, since only y is regrouped."""
+    rng = np.random.default_rng(seed)
+    p = _inputs(rng, N, T, HK, H, S)
+    scale = 1 / math.sqrt(S)
+    y_ref, st_ref = oracle.recurrence_seq(p["state"], p["q"], p["k"], p["v"], p["g"], p["beta"],
+                                          scale)
+    args = [dev(p[x]) for x in ("qh", "kh", "v", "g", "beta")]
+    st_t4, st_ex = dev(p["state"]), dev(p["state"])
+    y_t4 = torch.empty((N, T, H, S), device=DEV)
+    y_ex = torch.empty_like(y_t4)
+    sn_t4 = torch.empty((N, T, H, S, S), device=DEV) if with_snaps else None
+    sn_ex = torch.empty_like(sn_t4) if with_snaps else None
+    gdn.gdn_recurrence_seq_ex(st_t4, *args, y_t4, scale, sn_t4, variant=gdn.GDN_RECUR_T4)
+    gdn.gdn_recurrence_seq_ex(st_ex, *args, y_ex, scale, sn_ex, variant=gdn.GDN_RECUR_EXACT)
+    what = f"T4 scan N={N} T={T} HK={HK} H={H} S={S}"
+    assert_close(host(y_t4), y_ref, what + " y")
+    assert_close(host(st_t4), st_ref, what + " state")
+    assert torch.equal(st_t4, st_ex), what + ": state differs from the exact scan"
+    if with_snaps:
+        assert torch.equal(sn_t4, sn_ex), what + ": snapshots differ from the exact scan"
+    st_d = dev(p["state"])
+    for t in range(T):
+        y_d = torch.empty((N, H, S), device=DEV)
+        sl = lambda x: dev(np.ascontiguousarray(p[x][:, t]))
+        gdn.gdn_recurrence_ex(st_d, sl("qh"), sl("kh"), sl("v"), sl("g"), sl("beta"), y_d, scale,
+                              gdn.GDN_RECUR_T4)
+        assert torch.equal(y_t4[:, t], y_d), f"{what}: token {t} differs from the T4 decode"
+    assert torch.equal(st_t4, st_d), what + ": state differs from chained T4 decodes"
+
+
+@pytest.mark.parametrize("S", [32, 64, 128, 256])
+@pytest.mark.parametrize("T", [5, 70])
+def test_scan_t4(S, T):
+    """T = 5 takes the short scan (decode layout, no LDS), T = 70 the chunked
+    LDS scan with a ragged last chunk; k . q is formed in one shared order."""
+    _scan_t4_case(600 + S + T, 2, T, 2, 4, S, with_snaps=(T == 5))
+
+
+def test_scan_t4_many_blocks():
+    """768 scan blocks: the 32-token chunk variant, GQA 8 -> 32."""
+    _scan_t4_case(611, 3, 70, 8, 32, 128, with_snaps=False)
