@@ -99,7 +99,7 @@ constexpr int kTP = 16 + 4;     // LDS row pitch of a 16 x 16 scratch tile
 __global__ __launch_bounds__(256) void chunk_prep_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, float* __restrict__ ws, int n_tokens, int n_k_heads,
-    int n_v_heads, int n_chunks) {
+    int n_v_heads, int n_chunks, int v_groups) {
   constexpr int S = kChS, C = kChC;
   constexpr int AXT = 2 * C * kAP + 3 * 16 * kTP;   // A, X and three scratch tiles
   constexpr int SM = (C * kKP > AXT) ? C * kKP : AXT;
@@ -114,17 +114,22 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
   float* Xs = Sm + C * kAP;       // [C][kAP]
   float* Ts = Sm + 2 * C * kAP;   // [3][16][kTP]
 
-  // One block per (sequence, K-head, chunk). K K^T and Q K^T depend only on
-  // the K-head, so they are computed once and kept in registers; A, P and X,
-  // which take each V-head's gate and beta, are then formed for the V-heads
-  // kh, kh + HK, ... (V-head h reads K-head h mod HK) one after the other.
+  // One block per (sequence, K-head, V-head group, chunk). K K^T and Q K^T
+  // depend only on the K-head, so they are computed once and kept in
+  // registers; A, P and X, which take each V-head's gate and beta, are then
+  // formed for the block's V-heads kh + r*HK, r in [r0, r1) (V-head h reads
+  // K-head h mod HK), one after the other. The V-heads of a K-head are split
+  // over v_groups blocks only when one block per K-head would leave the chip
+  // short of blocks.
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int64_t kunit = blockIdx.x;                   // (n * HK + kh) * n_chunks + c
-  const int chunk = (int)(kunit % n_chunks);
-  const int64_t khead = kunit / n_chunks;             // n * HK + kh
+  const int64_t unit = blockIdx.x;                    // ((n * HK + kh) * v_groups + vg) * n_chunks + c
+  const int chunk = (int)(unit % n_chunks);
+  const int vg = (int)((unit / n_chunks) % v_groups);
+  const int64_t khead = unit / n_chunks / v_groups;   // n * HK + kh
   const int64_t n = khead / n_k_heads;
   const int kh = (int)(khead % n_k_heads);
-  const int gq = n_v_heads / n_k_heads;
+  const int per_group = n_v_heads / n_k_heads / v_groups;
+  const int r0 = vg * per_group, r1 = r0 + per_group;
   const int t0 = chunk * C;
   const int64_t kq_tok = (int64_t)n_k_heads * S;
   const float* kn = k + (n * n_tokens) * kq_tok + (int64_t)kh * S;
@@ -197,7 +202,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
       Bs[lane] = valid ? b_raw : 0.0f;
     }
   };
-  load_gate(kh);
+  load_gate(kh + r0 * n_k_heads);
 #pragma unroll
   for (int i = 0; i < KF; ++i) {
     const int f = (tid + 256 * i) * 4, t = f / S, col = f % S;
@@ -240,7 +245,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
   }
   __syncthreads();   // K no longer needed: A and X overwrite it
 
-  for (int r = 0; r < gq; ++r) {
+  for (int r = r0; r < r1; ++r) {
     // The lane indices of the body come from a copy the compiler cannot see
     // through, so its address arithmetic is redone per V-head instead of
     // being hoisted out of the loop, where it would hold some fifty
@@ -250,7 +255,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     const int g4r = (tid_r & 63) >> 4, l16r = tid_r & 15;
     const int h = kh + r * n_k_heads;
     const ChunkUnit u = chunk_unit(ws, ((n * n_v_heads + h) * n_chunks + chunk));
-    if (r + 1 < gq) load_gate(h + n_k_heads);   // lands during this V-head's work
+    if (r + 1 < r1) load_gate(h + n_k_heads);   // lands during this V-head's work
     if (tid_r < C) {
       u.gam[tid_r] = expf((float)Gs[tid_r]);
       u.ktf[tid_r] = expf((float)(Gs[C - 1] - Gs[tid_r]));
@@ -342,7 +347,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     // the next V-head's prefix sum; Gs and Bs were last read before the
     // barriers above, and the barrier below orders the X write-out before
     // the next iteration overwrites As and Xs
-    if (r + 1 < gq) {
+    if (r + 1 < r1) {
       prefix();
       __syncthreads();
     }
@@ -624,13 +629,21 @@ extern "C" int gdn_recurrence_seq_chunked(float* state, const float* q, const fl
     return GDN_EALIGN;
   const int n_chunks = (n_tokens + kChC - 1) / kChC;
   const int64_t units = (int64_t)n_seqs * n_v_heads * n_chunks;
-  const int64_t prep_blocks = (int64_t)n_seqs * n_k_heads * n_chunks;   // one per K-head and chunk
+  // one preparation block per K-head and chunk, unless that leaves fewer than
+  // four per CU: then the K-head's V-heads are split over v_groups blocks
+  // (the smallest divisor of the group size that fills the chip)
+  const int gq = n_v_heads / n_k_heads;
+  const int64_t k_units = (int64_t)n_seqs * n_k_heads * n_chunks;
+  int v_groups = 1;
+  while (v_groups < gq && (gq % v_groups != 0 || k_units * v_groups < 4 * (int64_t)cu_count()))
+    ++v_groups;
+  const int64_t prep_blocks = k_units * v_groups;
   const int64_t scan_blocks = (int64_t)n_seqs * n_v_heads * (kChS / kChR);
   if (units >= (int64_t(1) << 31) || scan_blocks >= (int64_t(1) << 31)) return GDN_ESIZE;
   hipStream_t s = as_stream(stream);
   float* ws = reinterpret_cast<float*>(workspace);
   hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)prep_blocks), dim3(256), 0, s, q, k, g, beta, ws,
-                     n_tokens, n_k_heads, n_v_heads, n_chunks);
+                     n_tokens, n_k_heads, n_v_heads, n_chunks, v_groups);
   int rc = launch_status();
   if (rc != GDN_OK) return rc;
   hipLaunchKernelGGL(chunk_scan_kernel, dim3((unsigned)scan_blocks), dim3(256), 0, s, state, q, k,
