@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "gdn.h"
 
 namespace gdn {
@@ -43,17 +45,19 @@ inline unsigned grid_for(int64_t items, int per_block) {
 
 // Compute units of the current device (queried once per device; 256 on
 // MI355X). Used only to choose between launch shapes, never for correctness.
+// The cache is atomic, so host threads that call the library concurrently
+// may each query it, but never read a torn value.
 inline int cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // The dispatcher hands workgroup b to XCD b % 8. This maps a block id to a
