@@ -17,7 +17,7 @@ from gpu_helpers import DEV, assert_close, dev, dev_bits, host, oracle_threads
 from linear_attention_ssm_recurrence_amd import gdn, inputs
 
 pytestmark = pytest.mark.gpu
-CASES = range(10)
+CASES = range(24)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -72,6 +72,7 @@ def test_random_scan(case):
     N = int(rng.integers(1, 3))
     T = int(rng.integers(1, 150 if S <= 128 else 40))
     snap = bool(rng.integers(0, 2)) and N * T * H * S * S <= (1 << 22)
+    variant = int(rng.integers(0, 2))       # exact or "T4" read-out
     p = _recurrence_inputs(rng, N, T, HK, H, S)
     scale = 1 / math.sqrt(S)
     y_ref, st_ref = oracle.recurrence_seq(p["state"], p["q"], p["k"], p["v"], p["g"], p["beta"],
@@ -80,8 +81,8 @@ def test_random_scan(case):
     y = torch.empty((N, T, H, S), device=DEV)
     snaps = torch.empty((N, T, H, S, S), device=DEV) if snap else None
     gdn.gdn_recurrence_seq_ex(st, dev(p["qh"]), dev(p["kh"]), dev(p["v"]), dev(p["g"]),
-                              dev(p["beta"]), y, scale, snaps)
-    what = f"scan N={N} T={T} HK={HK} H={H} S={S} snaps={snap}"
+                              dev(p["beta"]), y, scale, snaps, variant=variant)
+    what = f"scan N={N} T={T} HK={HK} H={H} S={S} snaps={snap} variant={variant}"
     assert_close(host(y), y_ref, what + " y")
     assert_close(host(st), st_ref, what + " state")
     if snap:
@@ -92,7 +93,7 @@ def test_random_scan(case):
 def test_random_chunked(case):
     rng = np.random.default_rng(12_000 + case)
     HK = int(rng.choice([1, 2, 4]))
-    H = HK * int(rng.choice([1, 2, 4]))
+    H = HK * int(rng.choice([1, 2, 3, 4, 8]))   # group sizes that split over blocks, or not
     N = int(rng.integers(1, 3))
     T = int(rng.integers(1, 300))
     S = 128
