@@ -36,6 +36,33 @@ def test_exports_every_header_symbol(lib):
         assert hasattr(lib, name)
 
 
+@pytest.mark.parametrize("std", ["c11", "c++17"])
+def test_c_consumer(lib, tmp_path, std):
+    """tests/abi_consumer.c, a plain C caller, builds as strict C11 and as
+    C++17 against include/gdn.h and include/gdn_probe.h, links against
+    libgdn.so (every declared function must resolve), and gets the expected
+    code from each entry point's argument checks through the header's own
+    prototypes. None of its calls passes validation, so nothing is launched."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc" if std == "c11" else "g++")
+    if cc is None:
+        pytest.skip("no host compiler")
+    here = os.path.dirname(os.path.abspath(__file__))
+    include = os.path.join(os.path.dirname(here), "include")
+    libdir = os.path.dirname(gdn.LIB_PATH)
+    exe = str(tmp_path / f"abi_consumer_{std.replace('+', 'p')}")
+    src = os.path.join(here, "abi_consumer.c")
+    cmd = [cc, f"-std={std}", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", include]
+    cmd += (["-x", "c++"] if std.startswith("c++") else []) + [src]
+    cmd += ["-L", libdir, "-lgdn", f"-Wl,-rpath,{libdir}", "-o", exe]
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stderr[-3000:]
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, run.stdout[-3000:] + run.stderr[-2000:]
+    assert run.stdout.strip().endswith("0 failures"), run.stdout
+
+
 def test_version_and_strerror(lib):
     assert lib.gdn_abi_version() == 1
     for code in range(6):
