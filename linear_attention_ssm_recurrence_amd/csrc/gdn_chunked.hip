@@ -190,9 +190,15 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     }
   };
   // cumulative log-decay (inclusive prefix sum across wave 0) and beta
+  // g below -1e4, -inf included (the gate's output when exp(A_log)
+  // overflows), enters the sum as -1e4: its decay is exactly 0 in fp32 either
+  // way, and a finite value keeps every difference Gc_t - Gc_s exact, where an
+  // infinite one would make the differences after it -inf - (-inf) = NaN.
+  // (The comparison leaves a NaN g NaN.)
   auto prefix = [&]() {
     if (wv == 0) {
-      double gc = valid ? (double)g_raw : 0.0;
+      const double gv = g_raw < -1.0e4f ? -1.0e4 : (double)g_raw;
+      double gc = valid ? gv : 0.0;
 #pragma unroll
       for (int off = 1; off < C; off <<= 1) {
         const double up = __shfl_up(gc, off);

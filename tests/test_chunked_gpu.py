@@ -140,3 +140,34 @@ def test_chunked_vs_sequential_gpu_prefill_shape():
                                           scale)
     assert_close(host(y_c)[:, :, heads], y_ref, "chunked y, sampled heads", rtol=RTOL_LONG_SCAN)
     assert_close(host(st_c)[:, heads], st_ref, "chunked state, sampled heads", rtol=RTOL_LONG_SCAN)
+
+
+def test_chunked_infinite_decay():
+    """g = -inf (the gate's output when exp(A_log) overflows) at the first, a
+    middle and the last position of chunks: the decay exp(g) is 0 there, so
+    the state restarts from k v^T terms alone, as in the oracle's sequential
+    scan. Strongly negative finite g around it as well."""
+    rng = np.random.default_rng(904)
+    N, T, HK, H = 2, 200, 2, 4
+    p = _case(rng, N, T, HK, H)
+    g = p["g"].copy()
+    g[0, 0, 0] = -np.inf          # first position of the sequence
+    g[0, 37, 1] = -np.inf         # inside a chunk
+    g[1, 63, 2] = -np.inf         # last position of a chunk
+    g[1, 64, 3] = -np.inf         # first position of the next chunk
+    g[0, 150:160, 2] = -1e30      # finite but far past underflow
+    g[1, 199, 0] = -np.inf        # last position of the sequence
+    p["g"] = g
+    scale = 1 / math.sqrt(128)
+    y_ref, st_ref = oracle.recurrence_seq(p["state"], p["q"], p["k"], p["v"], p["g"], p["beta"],
+                                          scale)
+    assert np.isfinite(y_ref).all() and np.isfinite(st_ref).all()
+    y, st = _gpu_chunked(p, scale)
+    assert_close(host(y), y_ref, "chunked y, infinite decay")
+    assert_close(host(st), st_ref, "chunked state, infinite decay")
+    st_s = dev(p["state"])
+    y_s = torch.empty_like(y)
+    gdn.gdn_recurrence_seq_ex(st_s, dev(p["qh"]), dev(p["kh"]), dev(p["v"]), dev(p["g"]),
+                              dev(p["beta"]), y_s, scale)
+    assert_close(host(y_s), y_ref, "sequential y, infinite decay")
+    assert_close(host(st_s), st_ref, "sequential state, infinite decay")
