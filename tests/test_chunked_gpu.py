@@ -171,3 +171,33 @@ def test_chunked_infinite_decay():
                               dev(p["beta"]), y_s, scale)
     assert_close(host(y_s), y_ref, "sequential y, infinite decay")
     assert_close(host(st_s), st_ref, "sequential state, infinite decay")
+
+
+def test_degenerate_inputs_both_scans():
+    """Degenerate values the method admits, through the chunked and the
+    sequential scan against the oracle: beta = 0 on a whole head (the state
+    only decays), zero k at some positions (the L2 norm of a zero vector),
+    zero q, g = 0 (no decay), and a head whose k is the same unit vector at
+    every position (every off-diagonal entry of a chunk's A is nonzero)."""
+    rng = np.random.default_rng(905)
+    N, T, HK, H = 1, 150, 4, 4
+    p = _case(rng, N, T, HK, H)
+    p["beta"][:, :, 0] = 0.0
+    for key in ("kh", "k"):
+        p[key][:, 10:14, 1] = 0.0
+        p[key][:, :, 3] = p[key][:, :1, 3]
+    for key in ("qh", "q"):
+        p[key][:, 70:90, 2] = 0.0
+    p["g"][:, 30:100, 1] = 0.0
+    scale = 1 / math.sqrt(128)
+    y_ref, st_ref = oracle.recurrence_seq(p["state"], p["q"], p["k"], p["v"], p["g"], p["beta"],
+                                          scale)
+    y, st = _gpu_chunked(p, scale)
+    assert_close(host(y), y_ref, "chunked y, degenerate inputs")
+    assert_close(host(st), st_ref, "chunked state, degenerate inputs")
+    st_s = dev(p["state"])
+    y_s = torch.empty_like(y)
+    gdn.gdn_recurrence_seq_ex(st_s, dev(p["qh"]), dev(p["kh"]), dev(p["v"]), dev(p["g"]),
+                              dev(p["beta"]), y_s, scale)
+    assert_close(host(y_s), y_ref, "sequential y, degenerate inputs")
+    assert_close(host(st_s), st_ref, "sequential state, degenerate inputs")
