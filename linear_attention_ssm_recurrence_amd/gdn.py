@@ -14,7 +14,9 @@ fallback path.
 from __future__ import annotations
 
 import ctypes
+import functools
 import glob
+import numbers
 import os
 import re
 
@@ -94,6 +96,20 @@ def strerror(code: int) -> str:
     return load_library().gdn_strerror(int(code)).decode()
 
 
+def _typed(fn):
+    """Reject, with TypeError, any argument that is not a tensor, a number,
+    None or a stream, before the function reads shapes from its arguments."""
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        for i, a in enumerate(list(args) + list(kwargs.values())):
+            if not (isinstance(a, (torch.Tensor, numbers.Number)) or a is None
+                    or hasattr(a, "cuda_stream")):
+                raise TypeError(f"{fn.__name__}: argument {i} must be a torch.Tensor or a "
+                                f"number, got {type(a).__name__}")
+        return fn(*args, **kwargs)
+    return wrapper
+
+
 def _call(name: str, *args) -> None:
     rc = getattr(load_library(), name)(*args)
     if rc != GDN_OK:
@@ -126,6 +142,7 @@ def _shape(t: torch.Tensor, shape: tuple, what: str) -> None:
 F32 = torch.float32
 
 
+@_typed
 def gdn_decay_gate(a, dt_bias, A_log, g, stream=None):
     """g[..., h] = -exp(A_log[h]) * softplus(a[..., h] + dt_bias[h])."""
     H = A_log.shape[0]
@@ -136,11 +153,13 @@ def gdn_decay_gate(a, dt_bias, A_log, g, stream=None):
           _stream(a, stream))
 
 
+@_typed
 def gdn_sigmoid(x, y, stream=None):
     _shape(y, x.shape, "y")
     _call("gdn_sigmoid", _ptr(x, F32, "x"), _ptr(y, F32, "y"), x.numel(), _stream(x, stream))
 
 
+@_typed
 def gdn_l2norm_gqa(x, out, eps=1e-6, stream=None):
     """x [..., HK, D] -> out [..., H, D]; V-head vh reads K-head vh mod HK."""
     HK, D = x.shape[-2:]
@@ -151,6 +170,7 @@ def gdn_l2norm_gqa(x, out, eps=1e-6, stream=None):
           float(eps), _stream(x, stream))
 
 
+@_typed
 def gdn_conv1d_silu(x, w, conv_state, out, stream=None):
     """x, out [N][C]; w [C][K]; conv_state [N][C][K-1] updated in place."""
     N, C = x.shape
@@ -162,6 +182,7 @@ def gdn_conv1d_silu(x, w, conv_state, out, stream=None):
           _ptr(out, F32, "out"), N, C, K, _stream(x, stream))
 
 
+@_typed
 def gdn_conv1d_silu_seq(x, w, conv_state, out, stream=None):
     """x, out [N][T][C]; w [C][K]; conv_state [N][C][K-1] updated in place."""
     N, T, C = x.shape
@@ -174,6 +195,7 @@ def gdn_conv1d_silu_seq(x, w, conv_state, out, stream=None):
           _stream(x, stream))
 
 
+@_typed
 def gdn_recurrence(state, q, k, v, g, beta, y, scale, stream=None):
     """state [N][H][S][S] in place; q, k, v, y [N][H][S]; g, beta [N][H]."""
     N, H, S = q.shape
@@ -187,6 +209,7 @@ def gdn_recurrence(state, q, k, v, g, beta, y, scale, stream=None):
           N, H, S, float(scale), _stream(q, stream))
 
 
+@_typed
 def gdn_recurrence_seq(state, q, k, v, g, beta, y, scale, stream=None):
     """state [N][H][S][S] in place; q, k, v, y [N][T][H][S]; g, beta [N][T][H]."""
     N, T, H, S = q.shape
@@ -200,6 +223,7 @@ def gdn_recurrence_seq(state, q, k, v, g, beta, y, scale, stream=None):
           N, T, H, S, float(scale), _stream(q, stream))
 
 
+@_typed
 def gdn_recurrence_ex(state, q, k, v, g, beta, y, scale, variant=GDN_RECUR_EXACT, stream=None):
     """state [N][H][S][S] in place; q, k [N][HK][S] (V-head h reads K-head
     h mod HK); v, y [N][H][S]; g, beta [N][H]."""
@@ -216,6 +240,7 @@ def gdn_recurrence_ex(state, q, k, v, g, beta, y, scale, variant=GDN_RECUR_EXACT
           N, HK, H, S, float(scale), int(variant), _stream(v, stream))
 
 
+@_typed
 def gdn_recurrence_seq_ex(state, q, k, v, g, beta, y, scale, snaps=None,
                           variant=GDN_RECUR_EXACT, stream=None):
     """state [N][H][S][S] in place; q, k [N][T][HK][S]; v, y [N][T][H][S];
@@ -238,6 +263,7 @@ def gdn_recurrence_seq_ex(state, q, k, v, g, beta, y, scale, snaps=None,
           N, T, HK, H, S, float(scale), int(variant), _stream(v, stream))
 
 
+@_typed
 def gdn_conv1d_silu_seq_ex(x, w, conv_state, out, snaps=None, stream=None):
     """gdn_conv1d_silu_seq with snaps None or [N][T][C][K-1] (history after
     each position)."""
@@ -255,6 +281,7 @@ def gdn_conv1d_silu_seq_ex(x, w, conv_state, out, snaps=None, stream=None):
           _stream(x, stream))
 
 
+@_typed
 def gdn_gated_rmsnorm(y, w, z, out, eps=1e-6, stream=None):
     """y, z, out [..., D]; w [D]."""
     D = w.shape[0]
@@ -266,6 +293,7 @@ def gdn_gated_rmsnorm(y, w, z, out, eps=1e-6, stream=None):
           _ptr(out, F32, "out"), y.numel() // max(D, 1), D, float(eps), _stream(y, stream))
 
 
+@_typed
 def gdn_decode_block_bf16(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out,
                           n_k_heads, scale, l2_eps=1e-6, eps=1e-6, stream=None):
     """One fused decode layer. qkv [N][C] and z [N][H][S] hold bf16 bit patterns
@@ -303,6 +331,7 @@ def gdn_prefill_workspace_bytes(n_seqs, n_tokens, n_k_heads, n_v_heads, state_si
                                                           state_size))
 
 
+@_typed
 def gdn_prefill_bf16(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out,
                      workspace, n_k_heads, scale, l2_eps=1e-6, eps=1e-6, stream=None, scan=None):
     """One layer over T positions. qkv [N][T][C] and z [N][T][H][S] hold bf16
@@ -340,6 +369,7 @@ def gdn_chunked_workspace_bytes(n_seqs, n_tokens, n_v_heads, state_size) -> int:
     return int(load_library().gdn_chunked_workspace_bytes(n_seqs, n_tokens, n_v_heads, state_size))
 
 
+@_typed
 def gdn_recurrence_seq_chunked(state, q, k, v, g, beta, y, scale, workspace, stream=None):
     """Chunked scan. state [N][H][S][S] in place; q, k [N][T][HK][S];
     v, y [N][T][H][S]; g, beta [N][T][H]; workspace a uint8 device tensor of
@@ -358,6 +388,7 @@ def gdn_recurrence_seq_chunked(state, q, k, v, g, beta, y, scale, workspace, str
           N, T, HK, H, S, float(scale), _stream(v, stream))
 
 
+@_typed
 def gdn_probe_fma(out, iters, a=0.999, b=1e-3, stream=None):
     """Measurement probe (not a step of the method): out is a float32 device
     tensor of n_blocks * 256 elements; runs n_blocks * 256 * iters * 32 flop

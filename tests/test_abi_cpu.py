@@ -262,3 +262,51 @@ def test_python_binding_rejects_cpu_tensors(lib):
     x = torch.zeros(4)
     with pytest.raises(ValueError):
         gdn.gdn_sigmoid(x, x)
+
+
+def test_python_binding_validation(lib):
+    """The binding checks shapes, devices and types before it calls the
+    library: a wrong shape or a CPU tensor raises ValueError, a non-tensor
+    TypeError, and nothing reaches the library (no GPU is needed here)."""
+    import torch
+    N, T, HK, H, S = 2, 3, 2, 4, 32
+    st = torch.zeros(N, H, S, S)
+    qh = torch.zeros(N, HK, S)
+    v = torch.zeros(N, H, S)
+    g = torch.zeros(N, H)
+    y = torch.zeros(N, H, S)
+    # shapes (checked first)
+    with pytest.raises(ValueError, match="state"):
+        gdn.gdn_recurrence_ex(torch.zeros(N, H, S, S + 1), qh, qh, v, g, g, y, 1.0)
+    with pytest.raises(ValueError, match="y"):
+        gdn.gdn_recurrence_ex(st, qh, qh, v, g, g, torch.zeros(N, H, S + 1), 1.0)
+    qs = torch.zeros(N, T, HK, S)
+    vs = torch.zeros(N, T, H, S)
+    gs = torch.zeros(N, T, H)
+    with pytest.raises(ValueError, match="snaps"):
+        gdn.gdn_recurrence_seq_ex(st, qs, qs, vs, gs, gs, vs.clone(), 1.0,
+                                  snaps=torch.zeros(N, T, H, S, S + 1))
+    with pytest.raises(ValueError, match="g"):
+        gdn.gdn_recurrence_seq_ex(st, qs, qs, vs, torch.zeros(N, T, H + 1), gs, vs.clone(), 1.0)
+    with pytest.raises(ValueError):
+        gdn.gdn_conv1d_silu_seq(torch.zeros(N, T, 8), torch.zeros(8, 4), torch.zeros(N, 8, 2),
+                                torch.zeros(N, T, 8))
+    with pytest.raises(ValueError):
+        gdn.gdn_gated_rmsnorm(torch.zeros(5, 32), torch.zeros(31), torch.zeros(5, 32),
+                              torch.zeros(5, 32))
+    with pytest.raises(ValueError, match="conv_dim"):
+        C, K = 2 * 16 * 128 + 32 * 128, 4
+        gdn.gdn_decode_block_bf16(torch.zeros(1, C + 8, dtype=torch.int16),
+                                  torch.zeros(1, 32, 128, dtype=torch.int16), torch.zeros(1, 32),
+                                  torch.zeros(1, 32), torch.zeros(C + 8, K), torch.zeros(32),
+                                  torch.zeros(32), torch.zeros(128), torch.zeros(1, C + 8, K - 1),
+                                  torch.zeros(1, 32, 128, 128), torch.zeros(1, 32, 128), 16, 0.1)
+    # devices and types (shapes right)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        gdn.gdn_recurrence_ex(st, qh, qh, v, g, g, y, 1.0)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ws = torch.zeros(gdn.gdn_chunked_workspace_bytes(N, T, H, 128), dtype=torch.uint8)
+        st128, q128, v128 = torch.zeros(N, H, 128, 128), torch.zeros(N, T, HK, 128), torch.zeros(N, T, H, 128)
+        gdn.gdn_recurrence_seq_chunked(st128, q128, q128, v128, gs, gs, v128.clone(), 1.0, ws)
+    with pytest.raises(TypeError):
+        gdn.gdn_sigmoid([0.0, 1.0], torch.zeros(2))
