@@ -98,14 +98,27 @@ def strerror(code: int) -> str:
 
 def _typed(fn):
     """Reject, with TypeError, any argument that is not a tensor, a number,
-    None or a stream, before the function reads shapes from its arguments."""
+    None or a stream, and, with ValueError, tensors on different devices,
+    before the function reads shapes from its arguments. The call then runs
+    with the tensors' GPU as the current device, which is the device the
+    library launches on."""
     @functools.wraps(fn)
     def wrapper(*args, **kwargs):
+        device = None
         for i, a in enumerate(list(args) + list(kwargs.values())):
-            if not (isinstance(a, (torch.Tensor, numbers.Number)) or a is None
-                    or hasattr(a, "cuda_stream")):
+            if isinstance(a, torch.Tensor):
+                if device is None:
+                    device = a.device
+                elif a.device != device:
+                    raise ValueError(f"{fn.__name__}: every tensor must be on the same device "
+                                     f"(argument {i} is on {a.device}, an earlier one on {device})")
+            elif not (isinstance(a, numbers.Number) or a is None or hasattr(a, "cuda_stream")):
                 raise TypeError(f"{fn.__name__}: argument {i} must be a torch.Tensor or a "
                                 f"number, got {type(a).__name__}")
+        if (device is not None and device.type == "cuda" and device.index is not None
+                and device.index != torch.cuda.current_device()):
+            with torch.cuda.device(device):
+                return fn(*args, **kwargs)
         return fn(*args, **kwargs)
     return wrapper
 

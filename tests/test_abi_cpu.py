@@ -310,3 +310,5 @@ def test_python_binding_validation(lib):
         gdn.gdn_recurrence_seq_chunked(st128, q128, q128, v128, gs, gs, v128.clone(), 1.0, ws)
     with pytest.raises(TypeError):
         gdn.gdn_sigmoid([0.0, 1.0], torch.zeros(2))
+    with pytest.raises(ValueError, match="same device"):
+        gdn.gdn_sigmoid(torch.zeros(2), torch.zeros(2, device="meta"))
