@@ -14,7 +14,9 @@ The same line carries the other workloads of the hot path ("legs"):
               sequential scan timed beside it); tokens/s
   block       64 sequences x 48 layers of the fused bf16 decode layer (conv,
               L2 norm + GQA repeat 16 -> 32, gate, sigmoid, recurrence, gated
-              RMSNorm), one launch per layer; ms per 48-layer step
+              RMSNorm), one launch per layer; ms per 48-layer step, for the
+              layer split over 64-row workgroups (gdn_decode_block_bf16_ex)
+              and, beside it, the one-workgroup-per-K-head layer
   decode_full the headline batch with its per-token glue launched too
               (decay gate, sigmoid, L2 norm + GQA of q and k) before the
               recurrence
@@ -421,6 +423,15 @@ def run_single(torch, gdn, inputs, steps, warmup):
                                   b_in["conv_state"], b_in["state"], b_out, HK, wb.scale,
                                   wb.l2_eps, wb.eps)
 
+    ws1 = torch.zeros(gdn.gdn_decode_block_workspace_bytes(1, HK, H), dtype=torch.uint8,
+                      device="cuda")
+
+    def fused_split():
+        gdn.gdn_decode_block_bf16_ex(b_in["qkv"], b_in["z"], b_in["a"], b_in["b"],
+                                     b_in["conv_w"], b_in["A_log"], b_in["dt_bias"],
+                                     b_in["norm_w"], b_in["conv_state"], b_in["state"], b_out,
+                                     ws1, HK, wb.scale, wb.l2_eps, wb.eps)
+
     def eager_us(fn):
         for _ in range(warmup):
             fn()
@@ -468,6 +479,9 @@ def run_single(torch, gdn, inputs, steps, warmup):
          "three_kernels_us_eager": eager_us(three),
          "fused_bf16_layer_us_warm": graph_us(fused), "fused_bf16_layer_us_flushed": cold_us(fused, reps),
          "fused_bf16_layer_us_eager": eager_us(fused),
+         "fused_bf16_layer_split_us_warm": graph_us(fused_split),
+         "fused_bf16_layer_split_us_flushed": cold_us(fused_split, reps),
+         "fused_bf16_layer_split_us_eager": eager_us(fused_split),
          "three_kernels_algorithmic_bytes": alg}
     r["three_kernels_GBps_flushed"] = alg / (r["three_kernels_us_flushed"] * 1e-6) / 1e9
     return r
@@ -527,27 +541,43 @@ def run_block(torch, gdn, inputs, steps, warmup):
         log(f"block: {len(layers)}/{Lyr} layers resident")
     torch.cuda.synchronize()
 
-    def step():
+    ws = torch.zeros(gdn.gdn_decode_block_workspace_bytes(N, HK, H), dtype=torch.uint8,
+                     device="cuda")
+
+    def step_split():
+        for t in layers:
+            gdn.gdn_decode_block_bf16_ex(t["qkv"], t["z"], t["a"], t["b"], t["conv_w"],
+                                         t["A_log"], t["dt_bias"], t["norm_w"], t["conv_state"],
+                                         t["state"], t["out"], ws, HK, w.scale, w.l2_eps, w.eps)
+
+    def step_one():
         for t in layers:
             gdn.gdn_decode_block_bf16(t["qkv"], t["z"], t["a"], t["b"], t["conv_w"], t["A_log"],
                                       t["dt_bias"], t["norm_w"], t["conv_state"], t["state"],
                                       t["out"], HK, w.scale, w.l2_eps, w.eps)
 
-    for _ in range(warmup):
-        step()
-    with Timer(torch) as tm:
-        for _ in range(steps):
+    times = {}
+    for name, step in (("split", step_split), ("one", step_one)):
+        for _ in range(warmup):
             step()
-    ms = tm.wall_ms / steps
+        with Timer(torch) as tm:
+            for _ in range(steps):
+                step()
+        times[name] = tm.wall_ms / steps
+    ms = times["split"]
     nbytes = Lyr * block_layer_bytes(N, H, HK, S, K)
     return {
         "workload": "fused bf16 decode layer: 64 sequences x 48 layers, 16 -> 32 heads, S=128, "
-                    "C=8192, K=4, one launch per layer",
+                    "C=8192, K=4, one launch per layer (gdn_decode_block_bf16_ex: 64-row "
+                    "workgroups)",
         "ms_per_step": ms,
         "launches_per_step": Lyr,
         "GBps": nbytes / (ms * 1e-3) / 1e9,
         "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "algorithmic_bytes_per_step": nbytes,
+        "one_workgroup_per_k_head_ms_per_step": times["one"],
+        "one_workgroup_per_k_head_frac_hbm_peak":
+            nbytes / (times["one"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
     }
 
 

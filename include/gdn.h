@@ -248,6 +248,37 @@ int gdn_decode_block_bf16(const uint16_t *qkv, const uint16_t *z, const float *a
                           void *stream);
 
 /*
+ * Workspace, in bytes, that gdn_decode_block_bf16_ex needs (0 for invalid
+ * sizes): one 32-bit counter per (sequence, K-head) and per (sequence,
+ * V-head).
+ */
+size_t gdn_decode_block_workspace_bytes(int n_seqs, int n_k_heads, int n_v_heads);
+
+/*
+ * The decode layer of gdn_decode_block_bf16 (same steps, same arguments,
+ * same results bit for bit), with the state of each V-head split over
+ * workgroups of 64 rows instead of one workgroup per K-head: faster when
+ * the state streams from HBM. Each workgroup convolves and normalises the
+ * q and k of its K-head itself; the last workgroup of a K-head to read
+ * their history rolls it, and the last workgroup of a V-head applies the
+ * gated norm, both found through counters in the workspace.
+ *   workspace  caller-owned device memory of at least
+ *              gdn_decode_block_workspace_bytes(...) bytes, 4-byte aligned,
+ *              ZERO before the first call; every completed call leaves it
+ *              zero again. Calls that may run at the same time (on
+ *              different streams) need workspaces of their own.
+ *   other arguments as gdn_decode_block_bf16.
+ * Errors: as gdn_decode_block_bf16; also GDN_ENULL (workspace NULL),
+ * GDN_ESIZE (workspace too small), GDN_EALIGN (workspace not 4-byte aligned).
+ */
+int gdn_decode_block_bf16_ex(const uint16_t *qkv, const uint16_t *z, const float *a,
+                             const float *b, const float *conv_w, const float *A_log,
+                             const float *dt_bias, const float *norm_w, float *conv_state,
+                             float *state, float *out, void *workspace, size_t workspace_bytes,
+                             int n_seqs, int n_k_heads, int n_v_heads, int state_size,
+                             int conv_kernel, float scale, float l2_eps, float eps, void *stream);
+
+/*
  * Workspace, in bytes, that gdn_prefill_bf16 and gdn_prefill_bf16_ex (either
  * scan) need for these sizes (0 for invalid sizes): normalised q and k per
  * K-head, v, g, beta and y, fp32, and the chunked scan's workspace.

@@ -232,6 +232,286 @@ static int launch_block_k(int K, const uint16_t* qkv, const uint16_t* z, const f
   return GDN_EUNSUPPORTED;
 }
 
+
+// ---------------------------------------------------------------------------
+// The same layer split over 64-row workgroups (gdn_decode_block_bf16_ex).
+//
+// A workgroup of 8 waves owns 64 state rows of one V-head (8 rows per wave,
+// the batched decode kernel's shape): the GQ*S/64 workgroups of a (sequence,
+// K-head) group each hold a quarter or half of the state the single-workgroup
+// kernel above holds, so four of them fit a CU at once and the state streams
+// as in the plain decode (measured at 64 sequences x 16 -> 32 heads: 47.3 us
+// per layer against 50.9 us). Every workgroup convolves and L2-normalises the
+// q and k of its K-head itself (from the same old history; 256 channels, a
+// few KB of L2 reads), and the conv channels of v are split by row, so each
+// v channel has one owner. Two steps need the whole group or the whole head,
+// and each is taken by the last workgroup to arrive at a counter in the
+// caller's workspace, so no workgroup ever waits for another:
+//   * the q/k history of the K-head is rolled by the last of the group's
+//     workgroups to count itself; each counts itself only after its own reads
+//     of that history have returned (their values were consumed before its
+//     first barrier), so no read can see the rolled history;
+//   * the gated norm of a V-head needs all S read-outs: each workgroup stores
+//     its rows' y to out with device-coherent stores and waits for them before
+//     it counts itself; the last of the head's workgroups reads the head's y
+//     back with device-coherent loads and writes the normalised row.
+// The last arriver resets its counter to zero, so the workspace is zero again
+// when the kernel ends. The arithmetic is the single-workgroup kernel's, step
+// by step and in the same order (the norm's sum of squares is row_sumsq's lane
+// order), so the two kernels agree bit for bit.
+// ---------------------------------------------------------------------------
+constexpr int kSplitRows = 64;   // state rows per workgroup
+constexpr int kSplitWaves = 8;   // 8 rows per wave
+
+template <int GQ, int K>
+__global__ __launch_bounds__(64 * kSplitWaves) void decode_block_split_kernel(
+    const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ z, const float* __restrict__ a,
+    const float* __restrict__ b, const float* __restrict__ conv_w,
+    const float* __restrict__ A_log, const float* __restrict__ dt_bias,
+    const float* __restrict__ norm_w, float* __restrict__ conv_state, float* __restrict__ state,
+    float* __restrict__ out, unsigned* __restrict__ counters, int64_t n_groups, int n_k_heads,
+    float scale, float l2_eps, float eps) {
+  constexpr int S = kBlockS;
+  using Lay = RecurLayout<S>;
+  constexpr int E = Lay::E, L = Lay::L, G = Lay::G;
+  constexpr int RW = kSplitRows / kSplitWaves;   // rows per wave
+  constexpr int IT = RW / G;                      // row groups per wave
+  constexpr int CPH = S / kSplitRows;             // workgroups per V-head
+  constexpr int P = GQ * CPH;                     // workgroups per (sequence, K-head)
+  constexpr int NCH = 2 * S + kSplitRows;         // q and k of kh, v of the rows
+  constexpr int TPB = 64 * kSplitWaves;
+  static_assert(NCH <= TPB && RW % G == 0 && CPH > 1, "one channel per thread; whole row groups");
+  static_assert(IT * E / 4 < 16, "the state stores must fit the vmcnt field");
+
+  __shared__ float co[NCH];          // conv output: q | k | v of the rows
+  __shared__ float zs[S], ws[S];     // silu input and weight of the head's norm
+  __shared__ float gate_d, gate_b;   // exp(g), beta
+  __shared__ int qk_last;
+
+  // workgroup -> (group = n * HK + kh, part); the P parts of a group are
+  // numbered onto one XCD, so the group's q/k reads after the first hit its L2
+  const int64_t blk = blockIdx.x;
+  const int64_t grp = (blk / (kXcds * P)) * kXcds + blk % kXcds;
+  const int part = (int)((blk / kXcds) % P);
+  if (grp >= n_groups) return;   // the whole workgroup, before any barrier
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int n_v_heads = GQ * n_k_heads;
+  const int key_dim = n_k_heads * S;
+  const int64_t C = 2 * (int64_t)key_dim + (int64_t)n_v_heads * S;
+  const int kh = (int)(grp % n_k_heads);
+  const int64_t n = grp / n_k_heads;
+  const int chunk = part % CPH;
+  const int vh = kh + (part / CPH) * n_k_heads;
+  const int64_t pair = n * n_v_heads + vh;
+  unsigned* cnt_group = counters + grp;
+  unsigned* cnt_head = counters + n_groups + pair;
+
+  // 0. conv input of this thread's channel, gate and norm inputs, then the
+  //    state rows (loads issued after the state would wait for all of it)
+  float wc[K], hist[K - 1], xv = 0.0f;
+  float* csp = nullptr;
+  const bool conv_lane = tid < NCH;
+  if (conv_lane) {
+    int64_t c;
+    if (tid < S) c = (int64_t)kh * S + tid;
+    else if (tid < 2 * S) c = key_dim + (int64_t)kh * S + (tid - S);
+    else c = 2 * (int64_t)key_dim + (int64_t)vh * S + chunk * kSplitRows + (tid - 2 * S);
+#pragma unroll
+    for (int u = 0; u < K; ++u) wc[u] = conv_w[c * K + u];
+    csp = conv_state + (n * C + c) * (K - 1);
+#pragma unroll
+    for (int u = 0; u < K - 1; ++u) hist[u] = csp[u];
+    xv = bf16_to_float(qkv[n * C + c]);
+  }
+  const bool gate_lane = (wv == 5 && lane == 0);
+  float ga = 0.0f, gdt = 0.0f, gal = 0.0f, gb = 0.0f;
+  if (gate_lane) {
+    ga = a[pair];
+    gdt = dt_bias[vh];
+    gal = A_log[vh];
+    gb = b[pair];
+  }
+  static_assert(S / 4 <= 64, "one float4 group of the norm row per lane");
+  const bool norm_lane = (wv == 6 && lane < S / 4);
+  uint2 zb = make_uint2(0u, 0u);
+  float4 nw = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (norm_lane) {
+    zb = *reinterpret_cast<const uint2*>(z + pair * S + 4 * lane);
+    nw = load4(norm_w + 4 * lane);
+  }
+  const int p = lane % L;
+  const int row0 = chunk * kSplitRows + wv * RW + lane / L;
+  float* sp = state + pair * (int64_t)S * S;
+  float4 raw[IT][E / 4];
+#pragma unroll
+  for (int it = 0; it < IT; ++it)
+#pragma unroll
+    for (int m = 0; m < E / 4; ++m)
+      raw[it][m] = load4_stream(sp + (int64_t)(row0 + it * G) * S + 4 * (p + L * m));
+
+  // 1. conv; the rows' own v channels roll their history at once
+  if (conv_lane) {
+    co[tid] = conv_point<K>(xv, hist, wc);
+    if (tid >= 2 * S) {
+#pragma unroll
+      for (int u = 0; u + 1 < K - 1; ++u) csp[u] = hist[u + 1];
+      csp[K - 2] = xv;
+    }
+  }
+  if (norm_lane) {
+    zs[4 * lane + 0] = bf16_to_float((uint16_t)(zb.x & 0xFFFFu));
+    zs[4 * lane + 1] = bf16_to_float((uint16_t)(zb.x >> 16));
+    zs[4 * lane + 2] = bf16_to_float((uint16_t)(zb.y & 0xFFFFu));
+    zs[4 * lane + 3] = bf16_to_float((uint16_t)(zb.y >> 16));
+    store4(ws + 4 * lane, nw);
+  }
+  __syncthreads();
+
+  // 2. L2 norm of q (wave 0) and k (wave 1); gate and beta (wave 5)
+  if (wv < 2) {
+    float* x = co + wv * S;
+    const float ss = row_sumsq(x, S / 4, lane);
+    const float norm = sqrtf(ss);
+    const float inv = 1.0f / (norm > l2_eps ? norm : l2_eps);
+    for (int m = lane; m < S / 4; m += 64) {
+      float4 v = load4(x + 4 * m);
+      v.x = v.x * inv;
+      v.y = v.y * inv;
+      v.z = v.z * inv;
+      v.w = v.w * inv;
+      store4(x + 4 * m, v);
+    }
+  } else if (gate_lane) {
+    const float gv = decay_gate(ga, gdt, gal);
+    gate_d = expf(gv);
+    gate_b = sigmoid(gb);
+  }
+  __syncthreads();
+
+  // Every read of the group's shared q/k history by this workgroup returned
+  // before the first barrier: count the workgroup. Wave 4 waits for the
+  // count where it waits for its state rows anyway; the result is used after
+  // the step.
+  unsigned group_old = 0u;
+  if (wv == 4 && lane == 0)
+    group_old = __hip_atomic_fetch_add(cnt_group, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // 3. delta-rule step on this wave's rows; y is published before the state
+  //    goes back
+  float* yrow = out + pair * S;
+  {
+    float kk[E], qq[E];
+    load_row_part<E, L>(co + S, p, kk);
+    load_row_part<E, L>(co, p, qq);
+    const float d = gate_d;
+    const float bt = gate_b;
+    const float* vv = co + 2 * S - chunk * kSplitRows;   // v of row j is vv[j]
+    float r[IT][E];
+    float yj[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      unpack<E>(raw[it], r[it]);
+      yj[it] = delta_rule_step<E, L>(r[it], kk, qq, vv[row0 + it * G], d, bt, scale);
+    }
+    if (p == 0) {
+#pragma unroll
+      for (int it = 0; it < IT; ++it)
+        __hip_atomic_store(yrow + row0 + it * G, yj[it], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      float* rp = sp + (int64_t)(row0 + it * G) * S;
+#pragma unroll
+      for (int m = 0; m < E / 4; ++m)
+        store4_stream(rp + 4 * (p + L * m), make_float4(r[it][4 * m], r[it][4 * m + 1],
+                                                        r[it][4 * m + 2], r[it][4 * m + 3]));
+    }
+    // Vector memory operations complete in issue order: with the IT*E/4 state
+    // stores still allowed in flight, the y stores issued before them are done.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt((IT * E / 4) | (7 << 4) | (15 << 8));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  }
+  if (wv == 4 && lane == 0) {
+    qk_last = (group_old == (unsigned)(P - 1));
+    if (group_old == (unsigned)(P - 1))
+      __hip_atomic_store(cnt_group, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+
+  // the group's last workgroup rolls the q/k history (every other one has read it)
+  if (qk_last && tid < 2 * S) {
+#pragma unroll
+    for (int u = 0; u + 1 < K - 1; ++u) csp[u] = hist[u + 1];
+    csp[K - 2] = xv;
+  }
+
+  // 4. every wave's y has reached memory. Wave 0 counts the workgroup for its
+  //    V-head; the head's last workgroup applies the gated norm to all S rows.
+  if (wv != 0) return;
+  unsigned head_old = 0u;
+  if (lane == 0) {
+    head_old = __hip_atomic_fetch_add(cnt_head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (head_old == (unsigned)(CPH - 1))
+      __hip_atomic_store(cnt_head, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  head_old = __builtin_amdgcn_readfirstlane(head_old);
+  if (head_old != (unsigned)(CPH - 1)) return;
+  // the sum of squares in row_sumsq's order: lane m holds entries 4m..4m+3
+  float y4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float ss = 0.0f;
+  if (lane < S / 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      y4[e] = __hip_atomic_load(yrow + 4 * lane + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(y4[e], y4[e], ss);
+  }
+  ss = group_sum<64>(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)S + eps);
+  if (lane < S / 4) {
+    const float4 w4 = load4(ws + 4 * lane);
+    float4 o;
+    o.x = y4[0] * inv * w4.x * silu(zs[4 * lane + 0]);
+    o.y = y4[1] * inv * w4.y * silu(zs[4 * lane + 1]);
+    o.z = y4[2] * inv * w4.z * silu(zs[4 * lane + 2]);
+    o.w = y4[3] * inv * w4.w * silu(zs[4 * lane + 3]);
+    store4(yrow + 4 * lane, o);
+  }
+}
+
+template <int GQ, int K>
+static int launch_block_split(const uint16_t* qkv, const uint16_t* z, const float* a,
+                              const float* b, const float* conv_w, const float* A_log,
+                              const float* dt_bias, const float* norm_w, float* conv_state,
+                              float* state, float* out, unsigned* counters, int64_t groups,
+                              int n_k_heads, float scale, float l2_eps, float eps, hipStream_t s) {
+  constexpr int P = GQ * (kBlockS / kSplitRows);
+  const int64_t blocks = ((groups + kXcds - 1) / kXcds) * kXcds * P;
+  hipLaunchKernelGGL((decode_block_split_kernel<GQ, K>), dim3((unsigned)blocks),
+                     dim3(64 * kSplitWaves), 0, s, qkv, z, a, b, conv_w, A_log, dt_bias, norm_w,
+                     conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps);
+  return launch_status();
+}
+
+template <int GQ>
+static int launch_block_split_k(int K, const uint16_t* qkv, const uint16_t* z, const float* a,
+                                const float* b, const float* conv_w, const float* A_log,
+                                const float* dt_bias, const float* norm_w, float* conv_state,
+                                float* state, float* out, unsigned* counters, int64_t groups,
+                                int n_k_heads, float scale, float l2_eps, float eps, hipStream_t s) {
+  switch (K) {
+    case 2: return launch_block_split<GQ, 2>(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps, s);
+    case 3: return launch_block_split<GQ, 3>(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps, s);
+    case 4: return launch_block_split<GQ, 4>(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps, s);
+  }
+  return GDN_EUNSUPPORTED;
+}
+
 }  // namespace gdn
 
 using namespace gdn;
@@ -264,6 +544,62 @@ extern "C" int gdn_decode_block_bf16(const uint16_t* qkv, const uint16_t* z, con
     case 1: return launch_block_k<1>(conv_kernel, qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, n_seqs, n_k_heads, scale, l2_eps, eps, s);
     case 2: return launch_block_k<2>(conv_kernel, qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, n_seqs, n_k_heads, scale, l2_eps, eps, s);
     case 4: return launch_block_k<4>(conv_kernel, qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, n_seqs, n_k_heads, scale, l2_eps, eps, s);
+  }
+  return GDN_EUNSUPPORTED;
+}
+
+
+// Counters of gdn_decode_block_bf16_ex: one per (sequence, K-head) group and
+// one per (sequence, V-head).
+static bool block_counters(int n_seqs, int n_k_heads, int n_v_heads, int64_t* count) {
+  int64_t groups, heads;
+  if (!mul_ok(n_seqs, n_k_heads, &groups) || !mul_ok(n_seqs, n_v_heads, &heads)) return false;
+  *count = groups + heads;
+  return true;
+}
+
+extern "C" size_t gdn_decode_block_workspace_bytes(int n_seqs, int n_k_heads, int n_v_heads) {
+  if (n_seqs < 0 || n_k_heads <= 0 || n_v_heads <= 0 || n_v_heads % n_k_heads != 0) return 0;
+  int64_t count;
+  if (!block_counters(n_seqs, n_k_heads, n_v_heads, &count)) return 0;
+  return (size_t)count * sizeof(unsigned);
+}
+
+extern "C" int gdn_decode_block_bf16_ex(const uint16_t* qkv, const uint16_t* z, const float* a,
+                                        const float* b, const float* conv_w, const float* A_log,
+                                        const float* dt_bias, const float* norm_w,
+                                        float* conv_state, float* state, float* out,
+                                        void* workspace, size_t workspace_bytes, int n_seqs,
+                                        int n_k_heads, int n_v_heads, int state_size,
+                                        int conv_kernel, float scale, float l2_eps, float eps,
+                                        void* stream) {
+  if (n_seqs < 0 || n_k_heads <= 0 || n_v_heads <= 0 || state_size <= 0 || conv_kernel <= 0)
+    return GDN_ESIZE;
+  if (n_v_heads % n_k_heads != 0) return GDN_ESIZE;
+  const int gq = n_v_heads / n_k_heads;
+  if (state_size != kBlockS || !(gq == 1 || gq == 2 || gq == 4)) return GDN_EUNSUPPORTED;
+  if (conv_kernel < 2 || conv_kernel > 4) return GDN_EUNSUPPORTED;
+  if (n_seqs == 0) return GDN_OK;
+  if (!qkv || !z || !a || !b || !conv_w || !A_log || !dt_bias || !norm_w || !conv_state ||
+      !state || !out || !workspace)
+    return GDN_ENULL;
+  int64_t pairs, st, count;
+  if (!mul_ok(n_seqs, n_v_heads, &pairs) || !mul_ok(pairs, (int64_t)state_size * state_size, &st))
+    return GDN_ESIZE;
+  if (!block_counters(n_seqs, n_k_heads, n_v_heads, &count)) return GDN_ESIZE;
+  if (workspace_bytes < (size_t)count * sizeof(unsigned)) return GDN_ESIZE;
+  const int64_t groups = (int64_t)n_seqs * n_k_heads;
+  const int64_t blocks = ((groups + kXcds - 1) / kXcds) * kXcds * gq * (kBlockS / kSplitRows);
+  if (blocks >= (int64_t(1) << 31)) return GDN_ESIZE;
+  if (!aligned16(state) || !aligned16(norm_w) || !aligned16(out)) return GDN_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(z) & 7u) != 0) return GDN_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return GDN_EALIGN;
+  hipStream_t s = as_stream(stream);
+  unsigned* counters = static_cast<unsigned*>(workspace);
+  switch (gq) {
+    case 1: return launch_block_split_k<1>(conv_kernel, qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps, s);
+    case 2: return launch_block_split_k<2>(conv_kernel, qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps, s);
+    case 4: return launch_block_split_k<4>(conv_kernel, qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps, s);
   }
   return GDN_EUNSUPPORTED;
 }

@@ -63,6 +63,7 @@ def load_library():
         "gdn_recurrence_seq": [P, P, P, P, P, P, P, I, I, I, I, F, P],
         "gdn_gated_rmsnorm": [P, P, P, P, L, I, F, P],
         "gdn_decode_block_bf16": [P] * 11 + [I] * 5 + [F] * 3 + [P],
+        "gdn_decode_block_bf16_ex": [P] * 12 + [ctypes.c_size_t] + [I] * 5 + [F] * 3 + [P],
         "gdn_prefill_bf16": [P] * 12 + [ctypes.c_size_t] + [I] * 6 + [F] * 3 + [P],
         "gdn_prefill_bf16_ex": [P] * 12 + [ctypes.c_size_t] + [I] * 6 + [F] * 3 + [I, P],
         "gdn_recurrence_seq_chunked": [P] * 8 + [ctypes.c_size_t] + [I] * 5 + [F, P],
@@ -79,6 +80,8 @@ def load_library():
     lib.gdn_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.gdn_chunked_workspace_bytes.argtypes = [I, I, I, I]
     lib.gdn_chunked_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_decode_block_workspace_bytes.argtypes = [I, I, I]
+    lib.gdn_decode_block_workspace_bytes.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -315,6 +318,41 @@ def gdn_decode_block_bf16(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_sta
     conv_state [N][C][K-1] and state [N][H][S][S] updated in place; out [N][H][S]."""
     N, H, S = z.shape
     C, K = conv_w.shape
+    _block_shapes(qkv, a, b, A_log, dt_bias, norm_w, conv_state, state, out, N, H, S, C, K,
+                  n_k_heads)
+    _call("gdn_decode_block_bf16", _ptr16(qkv, "qkv"), _ptr16(z, "z"), _ptr(a, F32, "a"),
+          _ptr(b, F32, "b"), _ptr(conv_w, F32, "conv_w"), _ptr(A_log, F32, "A_log"),
+          _ptr(dt_bias, F32, "dt_bias"), _ptr(norm_w, F32, "norm_w"),
+          _ptr(conv_state, F32, "conv_state"), _ptr(state, F32, "state"), _ptr(out, F32, "out"),
+          N, n_k_heads, H, S, K, float(scale), float(l2_eps), float(eps), _stream(z, stream))
+
+
+def gdn_decode_block_workspace_bytes(n_seqs, n_k_heads, n_v_heads) -> int:
+    return int(load_library().gdn_decode_block_workspace_bytes(n_seqs, n_k_heads, n_v_heads))
+
+
+@_typed
+def gdn_decode_block_bf16_ex(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state,
+                             out, workspace, n_k_heads, scale, l2_eps=1e-6, eps=1e-6,
+                             stream=None):
+    """gdn_decode_block_bf16 with the state split over 64-row workgroups.
+    Arguments as gdn_decode_block_bf16, plus workspace: a uint8 device tensor
+    of at least gdn_decode_block_workspace_bytes(N, n_k_heads, H) bytes that
+    is zero before the first call (every completed call leaves it zero)."""
+    N, H, S = z.shape
+    C, K = conv_w.shape
+    _block_shapes(qkv, a, b, A_log, dt_bias, norm_w, conv_state, state, out, N, H, S, C, K,
+                  n_k_heads)
+    _call("gdn_decode_block_bf16_ex", _ptr16(qkv, "qkv"), _ptr16(z, "z"), _ptr(a, F32, "a"),
+          _ptr(b, F32, "b"), _ptr(conv_w, F32, "conv_w"), _ptr(A_log, F32, "A_log"),
+          _ptr(dt_bias, F32, "dt_bias"), _ptr(norm_w, F32, "norm_w"),
+          _ptr(conv_state, F32, "conv_state"), _ptr(state, F32, "state"), _ptr(out, F32, "out"),
+          _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+          N, n_k_heads, H, S, K, float(scale), float(l2_eps), float(eps), _stream(z, stream))
+
+
+def _block_shapes(qkv, a, b, A_log, dt_bias, norm_w, conv_state, state, out, N, H, S, C, K,
+                  n_k_heads):
     _shape(qkv, (N, C), "qkv")
     for t, nm in ((a, "a"), (b, "b")):
         _shape(t, (N, H), nm)
@@ -326,11 +364,6 @@ def gdn_decode_block_bf16(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_sta
     _shape(out, (N, H, S), "out")
     if C != 2 * n_k_heads * S + H * S:
         raise ValueError(f"conv_dim {C} != 2*n_k_heads*S + n_v_heads*S")
-    _call("gdn_decode_block_bf16", _ptr16(qkv, "qkv"), _ptr16(z, "z"), _ptr(a, F32, "a"),
-          _ptr(b, F32, "b"), _ptr(conv_w, F32, "conv_w"), _ptr(A_log, F32, "A_log"),
-          _ptr(dt_bias, F32, "dt_bias"), _ptr(norm_w, F32, "norm_w"),
-          _ptr(conv_state, F32, "conv_state"), _ptr(state, F32, "state"), _ptr(out, F32, "out"),
-          N, n_k_heads, H, S, K, float(scale), float(l2_eps), float(eps), _stream(z, stream))
 
 
 def _ptr16(t: torch.Tensor, what: str) -> int:

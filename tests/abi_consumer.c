@@ -86,6 +86,16 @@ int main(void) {
                                0.1f, 1e-6f, 1e-6f, NULL),
          GDN_EUNSUPPORTED);
 
+  /* one counter per (sequence, K-head) and per (sequence, V-head) */
+  EXPECT(gdn_decode_block_workspace_bytes(2, 16, 32), (2L * 16 + 2L * 32) * 4);
+  EXPECT(gdn_decode_block_workspace_bytes(2, 16, 24), 0);
+  EXPECT(gdn_decode_block_bf16_ex(buf16, buf16, cf, cf, cf, cf, cf, cf, f, f, f, f, 16, 1, 16, 32,
+                                  128, 4, 0.1f, 1e-6f, 1e-6f, NULL),
+         GDN_ESIZE); /* workspace too small */
+  EXPECT(gdn_decode_block_bf16_ex(buf16, buf16, cf, cf, cf, cf, cf, cf, f, f, f, NULL, 4096, 1,
+                                  16, 32, 128, 4, 0.1f, 1e-6f, 1e-6f, NULL),
+         GDN_ENULL);
+
   EXPECT(gdn_prefill_workspace_bytes(1, 64, 16, 32, 128) > 0, 1);
   EXPECT(gdn_prefill_workspace_bytes(1, 64, 0, 32, 128), 0);
   EXPECT(gdn_prefill_bf16(buf16, buf16, cf, cf, cf, cf, cf, cf, f, f, f, f, 16, 1, 64, 16, 32,

@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_header_symbol(lib):
     names = gdn.header_symbols()
-    assert len(names) == 20, names
+    assert len(names) == 22, names
     out = os.popen(f"nm -D --defined-only {gdn.LIB_PATH}").read()
     exported = set(re.findall(r"\sT\s(gdn_\w+)", out))
     for name in names:
@@ -189,6 +189,34 @@ def test_block_validation(lib):
     assert call(state=FAKE_MIS) == gdn.GDN_EALIGN
     assert call(z=ctypes.c_void_p(0x10002)) == gdn.GDN_EALIGN
     assert call(first=NUL, state=NUL, n=0) == gdn.GDN_OK
+
+
+def test_block_ex_validation(lib):
+    f = lib.gdn_decode_block_bf16_ex
+    need = lib.gdn_decode_block_workspace_bytes(3, 16, 32)
+    assert need == (3 * 16 + 3 * 32) * 4
+    assert lib.gdn_decode_block_workspace_bytes(3, 16, 24) == 0   # 24 % 16 != 0
+    assert lib.gdn_decode_block_workspace_bytes(3, 0, 32) == 0
+    assert lib.gdn_decode_block_workspace_bytes(-1, 16, 32) == 0
+    assert lib.gdn_decode_block_workspace_bytes(0, 16, 32) == 0
+
+    def call(first=FAKE, state=FAKE, ws=FAKE, ws_bytes=need, n=3, HK=16, H=32, S=128, K=4,
+             z=FAKE):
+        return f(first, z, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, state, FAKE, ws, ws_bytes,
+                 n, HK, H, S, K, 0.1, 1e-6, 1e-6, NUL)
+
+    assert call(first=NUL) == gdn.GDN_ENULL
+    assert call(ws=NUL) == gdn.GDN_ENULL
+    assert call(ws_bytes=need - 1) == gdn.GDN_ESIZE
+    assert call(ws=ctypes.c_void_p(0x10002)) == gdn.GDN_EALIGN
+    assert call(n=-1) == gdn.GDN_ESIZE
+    assert call(HK=12) == gdn.GDN_ESIZE                 # 32 % 12 != 0
+    assert call(HK=4) == gdn.GDN_EUNSUPPORTED           # 8 V-heads per K-head
+    assert call(S=64) == gdn.GDN_EUNSUPPORTED
+    assert call(K=1) == gdn.GDN_EUNSUPPORTED
+    assert call(state=FAKE_MIS) == gdn.GDN_EALIGN
+    assert call(z=ctypes.c_void_p(0x10002)) == gdn.GDN_EALIGN
+    assert call(first=NUL, state=NUL, ws=NUL, n=0) == gdn.GDN_OK
 
 
 def test_prefill_validation(lib):

@@ -4,7 +4,9 @@ A caller that replays a captured decode step must get exactly what eager
 launches give: the same kernels run on the same data. The step (conv, the
 recurrence, the gated norm, and the fused bf16 layer) is captured once and
 replayed several times, with eager work and synchronisation between the
-replays, and every replay is compared with the eager result bit for bit.
+replays, and every replay is compared with the eager result bit for bit. The
+layer split over 64-row workgroups is captured too: its counters must be zero
+again after every replay, since no replay clears them.
 """
 import numpy as np
 import pytest
@@ -44,13 +46,17 @@ def test_decode_step_graph_replays_equal_eager():
     wb = inputs.WORKLOADS[4]
     lb = inputs.draw_block_layer(0, wb, n_seqs=3)
     b_in = {key: (_bits(val) if val.dtype == np.uint16 else dev(val)) for key, val in lb.items()}
+    ws = torch.zeros(gdn.gdn_decode_block_workspace_bytes(3, HK, H), dtype=torch.uint8,
+                     device=DEV)
 
     def fresh():
         return {"st": dev(d["state"]), "cs": dev(d["conv_state"]),
                 "bst": b_in["state"].clone(), "bcs": b_in["conv_state"].clone(),
                 "y": torch.empty((1, H, S), device=DEV), "out": torch.empty((1, H, S), device=DEV),
                 "co": torch.empty((1, w.conv_dim), device=DEV),
-                "bout": torch.empty((3, H, S), device=DEV)}
+                "bout": torch.empty((3, H, S), device=DEV),
+                "sst": b_in["state"].clone(), "scs": b_in["conv_state"].clone(),
+                "sout": torch.empty((3, H, S), device=DEV)}
 
     def step(b):
         gdn.gdn_conv1d_silu(x, cw, b["cs"], b["co"])
@@ -59,6 +65,10 @@ def test_decode_step_graph_replays_equal_eager():
         gdn.gdn_decode_block_bf16(b_in["qkv"], b_in["z"], b_in["a"], b_in["b"], b_in["conv_w"],
                                   b_in["A_log"], b_in["dt_bias"], b_in["norm_w"], b["bcs"],
                                   b["bst"], b["bout"], HK, wb.scale, wb.l2_eps, wb.eps)
+        gdn.gdn_decode_block_bf16_ex(b_in["qkv"], b_in["z"], b_in["a"], b_in["b"],
+                                     b_in["conv_w"], b_in["A_log"], b_in["dt_bias"],
+                                     b_in["norm_w"], b["scs"], b["sst"], b["sout"], ws, HK,
+                                     wb.scale, wb.l2_eps, wb.eps)
 
     replays = 4
     eager = fresh()
@@ -85,8 +95,11 @@ def test_decode_step_graph_replays_equal_eager():
     for r in range(replays):
         graph.replay()
         torch.cuda.synchronize()
-        for key in ("st", "cs", "out", "co", "bst", "bcs", "bout"):
+        for key in ("st", "cs", "out", "co", "bst", "bcs", "bout", "sst", "scs", "sout"):
             assert torch.equal(cap[key], ref[r][key]), f"replay {r}: {key} differs from eager"
+        assert int(ws.count_nonzero()) == 0, f"replay {r}: split-layer counters not zero"
+        for a, b in (("sst", "bst"), ("scs", "bcs"), ("sout", "bout")):
+            assert torch.equal(cap[a], cap[b]), f"replay {r}: split layer != one-workgroup layer"
         scratch = torch.randn(1 << 20, device=DEV)    # eager work between replays
         scratch.mul_(2.0)
         torch.cuda.synchronize()
