@@ -158,7 +158,8 @@ def test_gated_norm_rows_past_2g_elements():
     assert_close(host(out[pick]), oracle.gated_rmsnorm(y_s, host(w), z_s), "gated norm rows")
 
 
-def test_decode_block_state_past_2g_elements():
+@pytest.mark.parametrize("split", [False, True], ids=["one_workgroup", "split_64_rows"])
+def test_decode_block_state_past_2g_elements(split):
     N, HK, H, S, K = 4100, 16, 32, 128, 4
     C = 2 * HK * S + H * S
     assert N * H * S * S > TWO31
@@ -177,8 +178,15 @@ def test_decode_block_state_past_2g_elements():
                       st=host(state[n:n + 1])) for n in seqs}
     out = torch.empty((N, H, S), device=DEV)
     scale = 1 / math.sqrt(S)
-    gdn.gdn_decode_block_bf16(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out,
-                              HK, scale)
+    if split:
+        ws = torch.zeros(gdn.gdn_decode_block_workspace_bytes(N, HK, H), dtype=torch.uint8,
+                         device=DEV)
+        gdn.gdn_decode_block_bf16_ex(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state,
+                                     state, out, ws, HK, scale)
+        assert int(ws.count_nonzero()) == 0, "split layer: workspace not zero after the call"
+    else:
+        gdn.gdn_decode_block_bf16(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state,
+                                  state, out, HK, scale)
     for n in seqs:
         d = before[n]
         o_ref, cs_ref, st_ref = oracle.decode_block_bf16(
