@@ -144,7 +144,7 @@ def draw(w: Workload | int, seed: int | None = None, n_seqs: int | None = None,
 
 
 def draw_block_layer(layer: int, w: Workload | int = 4, n_seqs: int | None = None) -> dict:
-    """Raw draws for one layer of the bf16 decode block (config 4).
+    """Raw draws for one layer of the bf16 decode block (64 sequences x 48 layers).
 
     Returns qkv [N][C] and z [N][H][S] as bf16 bit patterns (uint16) plus
     float32 a, b [N][H], conv_w [C][K], A_log, dt_bias [H], norm_w [S],

@@ -70,7 +70,7 @@ def _gpu_steps(p, scale):
 # Recurrence
 # ---------------------------------------------------------------------------
 
-def test_tiny_scan_config0():
+def test_tiny_scan_1seq_2heads_s32_t8():
     """1 sequence, 2 heads, S = 32, 8 tokens, zero initial state."""
     w = inputs.WORKLOADS[0]
     p = prep_recurrence(inputs.draw(w), w)
@@ -109,7 +109,7 @@ def test_decode_shapes(S, N, H):
     assert_close(host(st), st_ref, f"decode state S={S}")
 
 
-def test_batched_decode_config2_full():
+def test_batched_decode_256seqs_full():
     """256 sequences x 32 V-heads x S = 128 (512 MiB of state), every element."""
     w = inputs.WORKLOADS[2]
     d = inputs.draw(w)
@@ -121,8 +121,8 @@ def test_batched_decode_config2_full():
     y = torch.empty((w.n_seqs, w.n_v_heads, w.state_size), dtype=torch.float32, device=DEV)
     q, k, v, g, b = (dev(sq(p[x])) for x in ("q", "k", "v", "g", "beta"))
     gdn.gdn_recurrence(st, q, k, v, g, b, y, w.scale)
-    assert_close(host(y), y_ref, "config2 y")
-    assert_close(host(st), st_ref, "config2 state")
+    assert_close(host(y), y_ref, "batched decode y")
+    assert_close(host(st), st_ref, "batched decode state")
     # same launch again from the same state: identical bits
     st2 = dev(p["state"])
     y2 = torch.empty_like(y)
@@ -130,7 +130,7 @@ def test_batched_decode_config2_full():
     assert torch.equal(st, st2) and torch.equal(y, y2), "decode is not deterministic"
 
 
-def test_scan_config3_full():
+def test_scan_4096_tokens_full():
     """1 sequence, 4096 tokens, 32 heads, S = 128, zero initial state; the final
     state must also equal 4096 chained decode launches."""
     w = inputs.WORKLOADS[3]
@@ -138,8 +138,8 @@ def test_scan_config3_full():
     p = prep_recurrence(d, w)
     y_ref, st_ref = oracle.recurrence_seq(p["state"], p["q"], p["k"], p["v"], p["g"], p["beta"], w.scale)
     y, st = _gpu_scan(p, w.scale)
-    assert_close(host(y), y_ref, "config3 y", rtol=RTOL_LONG_SCAN)
-    assert_close(host(st), st_ref, "config3 final state", rtol=RTOL_LONG_SCAN)
+    assert_close(host(y), y_ref, "4096-token scan y", rtol=RTOL_LONG_SCAN)
+    assert_close(host(st), st_ref, "4096-token scan final state", rtol=RTOL_LONG_SCAN)
     y2, st2 = _gpu_steps(p, w.scale)
     assert torch.equal(st, st2), "4096-token scan != 4096 chained decode launches (state bits)"
     assert torch.equal(y, y2), "4096-token scan != 4096 chained decode launches (y bits)"
@@ -184,7 +184,7 @@ def test_conv_shapes(K, N, T, C):
     assert torch.equal(cs2, cs)
 
 
-def test_conv_config3_full():
+def test_conv_4096x8192_full():
     """x [4096][8192] ~ N(0,1), w ~ N(0, 0.5), zero history."""
     w = inputs.WORKLOADS[3]
     d = inputs.draw(w)
@@ -192,8 +192,8 @@ def test_conv_config3_full():
     cs = dev(d["conv_state"])
     out = torch.empty(d["x"].shape, dtype=torch.float32, device=DEV)
     gdn.gdn_conv1d_silu_seq(dev(d["x"]), dev(d["conv_w"]), cs, out)
-    assert_close(host(out), out_ref, "config3 conv out")
-    assert np.array_equal(host(cs), cs_ref), "config3 conv history"
+    assert_close(host(out), out_ref, "conv 4096x8192 out")
+    assert np.array_equal(host(cs), cs_ref), "conv 4096x8192 history"
 
 
 # ---------------------------------------------------------------------------
@@ -248,7 +248,7 @@ def test_gated_rmsnorm(D):
     assert_close(host(out), oracle.gated_rmsnorm(y, w, z, 1e-6), f"gated norm D={D}")
 
 
-def test_single_decode_config1_stages_and_chain():
+def test_single_decode_one_seq_stages_and_chain():
     """Every stage at the single-decode shapes (16 -> 32 heads, S = 128,
     C = 8192), then the fp32 decode layer chained on the GPU against the
     chained oracle."""
@@ -259,29 +259,29 @@ def test_single_decode_config1_stages_and_chain():
     # stage by stage
     qg = torch.empty((1, 1, H, S), dtype=torch.float32, device=DEV)
     gdn.gdn_l2norm_gqa(dev(d["q_raw"]), qg, w.l2_eps)
-    assert_close(host(qg), p["q"], "config1 q l2norm+gqa")
+    assert_close(host(qg), p["q"], "one-sequence q l2norm+gqa")
     g = torch.empty((1, 1, H), dtype=torch.float32, device=DEV)
     gdn.gdn_decay_gate(dev(d["a"]), dev(d["dt_bias"]), dev(d["A_log"]), g)
-    assert_close(host(g), p["g"], "config1 gate")
+    assert_close(host(g), p["g"], "one-sequence gate")
     bt = torch.empty((1, 1, H), dtype=torch.float32, device=DEV)
     gdn.gdn_sigmoid(dev(d["b"]), bt)
-    assert_close(host(bt), p["beta"], "config1 beta")
+    assert_close(host(bt), p["beta"], "one-sequence beta")
     y_ref, st_ref = oracle.recurrence(p["state"], p["q"][:, 0], p["k"][:, 0], p["v"][:, 0],
                                       p["g"][:, 0], p["beta"][:, 0], w.scale)
     st = dev(p["state"])
     y = torch.empty((1, H, S), dtype=torch.float32, device=DEV)
     gdn.gdn_recurrence(st, dev(p["q"][:, 0]), dev(p["k"][:, 0]), dev(p["v"][:, 0]),
                        dev(p["g"][:, 0]), dev(p["beta"][:, 0]), y, w.scale)
-    assert_close(host(y), y_ref, "config1 y")
-    assert_close(host(st), st_ref, "config1 state")
+    assert_close(host(y), y_ref, "one-sequence y")
+    assert_close(host(st), st_ref, "one-sequence state")
     out = torch.empty((1, H, S), dtype=torch.float32, device=DEV)
     gdn.gdn_gated_rmsnorm(y, dev(d["norm_w"]), dev(d["z"][:, 0]), out, w.eps)
-    assert_close(host(out), oracle.gated_rmsnorm(host(y), d["norm_w"], d["z"][:, 0], w.eps), "config1 norm")
+    assert_close(host(out), oracle.gated_rmsnorm(host(y), d["norm_w"], d["z"][:, 0], w.eps), "one-sequence norm")
     co_ref, cs_ref = oracle.conv1d_silu(d["x"][:, 0], d["conv_w"], d["conv_state"])
     cs = dev(d["conv_state"])
     co = torch.empty((1, w.conv_dim), dtype=torch.float32, device=DEV)
     gdn.gdn_conv1d_silu(dev(d["x"][:, 0]), dev(d["conv_w"]), cs, co)
-    assert_close(host(co), co_ref, "config1 conv")
+    assert_close(host(co), co_ref, "one-sequence conv")
     assert np.array_equal(host(cs), cs_ref)
 
     # chained: conv -> split -> l2norm + gqa -> gate, beta -> recurrence -> norm
@@ -308,9 +308,9 @@ def test_single_decode_config1_stages_and_chain():
     gdn.gdn_recurrence(stc, qd, kdv, co[:, 2 * kd:].reshape(1, H, S).contiguous(), gdd, bdd, yc, w.scale)
     oc = torch.empty((1, H, S), dtype=torch.float32, device=DEV)
     gdn.gdn_gated_rmsnorm(yc, dev(d["norm_w"]), dev(d["z"][:, 0]), oc, w.eps)
-    assert_close(host(yc), yc_ref, "config1 chained y")
-    assert_close(host(stc), stc_ref, "config1 chained state")
-    assert_close(host(oc), oc_ref, "config1 chained out")
+    assert_close(host(yc), yc_ref, "one-sequence chained y")
+    assert_close(host(stc), stc_ref, "one-sequence chained state")
+    assert_close(host(oc), oc_ref, "one-sequence chained out")
 
 
 # ---------------------------------------------------------------------------
@@ -365,12 +365,12 @@ def _check_block(d, HK, scale, what):
 
 
 @pytest.mark.parametrize("layer", [0, 47])
-def test_block_config4_layers(layer):
+def test_block_64seq_layers(layer):
     """64 sequences, 16 K-heads -> 32 V-heads, S = 128, C = 8192, K = 4: one
     launch per layer, as the benchmark runs it."""
     w = inputs.WORKLOADS[4]
     d = inputs.draw_block_layer(layer)
-    _check_block(d, w.n_k_heads, w.scale, f"config4 layer {layer}")
+    _check_block(d, w.n_k_heads, w.scale, f"64-sequence block layer {layer}")
 
 
 @pytest.mark.parametrize("GQ", [1, 2, 4])
