@@ -4,7 +4,9 @@ within the tolerance (needs an MI355X).
 The fixed-shape parity files cover the workloads at their real sizes; this
 sweep draws many small, odd shapes (sequence, token and head counts, state
 sizes, conv widths, grouped-query ratios, head dims) from fixed seeds, so that
-ragged tails and unusual combinations are exercised too.
+ragged tails and unusual combinations are exercised too. The fused decode
+layer's family runs both of its kernels (one workgroup per K-head, and 64-row
+workgroups) on each case.
 """
 import math
 
@@ -178,3 +180,51 @@ def test_random_norms(case):
     got = torch.empty((n, H, D), device=DEV)
     gdn.gdn_l2norm_gqa(dev(x), got, 1e-6)
     assert_close(host(got), oracle.l2norm_gqa(x, H, 1e-6), f"l2norm n={n} HK={HK} H={H} D={D}")
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_random_decode_layer(case):
+    """Both fused decode layers on a random batch: the one-workgroup layer and
+    the layer split over 64-row workgroups, each against the oracle, and the
+    two bit for bit; the split layer's workspace is zero again afterwards."""
+    rng = np.random.default_rng(70_000 + case)
+    S = 128
+    HK = int(rng.integers(1, 7))
+    GQ = int(rng.choice([1, 2, 4]))
+    H = HK * GQ
+    K = int(rng.integers(2, 5))
+    N = int(rng.integers(1, 24))
+    C = 2 * HK * S + H * S
+    bits = lambda x: inputs.to_bf16_bits(x.astype(np.float32))
+    d = dict(qkv=bits(rng.standard_normal((N, C))), z=bits(rng.standard_normal((N, H, S))),
+             a=rng.standard_normal((N, H)).astype(np.float32),
+             b=rng.standard_normal((N, H)).astype(np.float32),
+             conv_w=(rng.standard_normal((C, K)) * 0.5).astype(np.float32),
+             A_log=rng.standard_normal(H).astype(np.float32),
+             dt_bias=(0.5 * rng.standard_normal(H)).astype(np.float32),
+             norm_w=(1 + 0.1 * rng.standard_normal(S)).astype(np.float32),
+             conv_state=rng.standard_normal((N, C, K - 1)).astype(np.float32),
+             state=(0.05 * rng.standard_normal((N, H, S, S))).astype(np.float32))
+    scale = 1 / math.sqrt(S)
+    o_ref, cs_ref, st_ref = oracle.decode_block_bf16(
+        d["qkv"], d["z"], d["a"], d["b"], d["conv_w"], d["A_log"], d["dt_bias"], d["norm_w"],
+        d["conv_state"], d["state"], HK, scale)
+    fixed = [dev(d[k]) for k in ("conv_w", "A_log", "dt_bias", "norm_w")]
+    step = [dev_bits(d["qkv"]), dev_bits(d["z"]), dev(d["a"]), dev(d["b"])]
+    ws = torch.zeros(gdn.gdn_decode_block_workspace_bytes(N, HK, H), dtype=torch.uint8, device=DEV)
+    results = []
+    for split in (False, True):
+        cs, st = dev(d["conv_state"]), dev(d["state"])
+        out = torch.empty((N, H, S), device=DEV)
+        if split:
+            gdn.gdn_decode_block_bf16_ex(*step, *fixed, cs, st, out, ws, HK, scale)
+        else:
+            gdn.gdn_decode_block_bf16(*step, *fixed, cs, st, out, HK, scale)
+        what = f"case {case} (N={N}, HK={HK}, GQ={GQ}, K={K}, split={split})"
+        assert_close(host(out), o_ref, f"{what} out")
+        assert_close(host(st), st_ref, f"{what} state")
+        assert np.array_equal(host(cs), cs_ref), f"{what} conv history"
+        results.append((out, st, cs))
+    for a, b, name in zip(results[0], results[1], ("out", "state", "conv history")):
+        assert torch.equal(a, b), f"case {case}: split layer != one-workgroup layer ({name} bits)"
+    assert int(ws.count_nonzero()) == 0, f"case {case}: workspace not zero after the call"
