@@ -2,7 +2,8 @@
 
 The decode, the scan and the fused layer are run on a side stream (with the
 default stream busy on other work) and on the default stream; the results
-must be identical bit for bit.
+must be identical bit for bit. The split decode layer also runs on two
+streams at once, each call with its own workspace.
 """
 import numpy as np
 import pytest
@@ -58,3 +59,43 @@ def test_side_stream_equals_default_stream():
     torch.cuda.synchronize()
     for a, b in zip(ref, got):
         assert torch.equal(a, b)
+
+
+def test_split_layer_on_two_streams_with_own_workspaces():
+    """Two split decode layers in flight at once on two streams (different
+    batches, each with its own workspace, as the header requires), repeated:
+    each equals the one-workgroup layer on the same inputs, and both
+    workspaces are zero afterwards."""
+    wb = inputs.WORKLOADS[4]
+    H, HK, S = wb.n_v_heads, wb.n_k_heads, wb.state_size
+    layers = [inputs.draw_block_layer(l, wb, n_seqs=n) for l, n in ((2, 24), (3, 40))]
+
+    def upload(lb):
+        return {key: (_bits(val) if val.dtype == np.uint16 else dev(val)) for key, val in lb.items()}
+
+    def call(fn, t, out, *extra):
+        fn(t["qkv"], t["z"], t["a"], t["b"], t["conv_w"], t["A_log"], t["dt_bias"], t["norm_w"],
+           t["conv_state"], t["state"], out, *extra, HK, wb.scale, wb.l2_eps, wb.eps)
+
+    ref, got, wss = [], [], []
+    for lb in layers:
+        n = lb["a"].shape[0]
+        r, g = upload(lb), upload(lb)
+        ref.append((r, torch.empty((n, H, S), device=DEV)))
+        got.append((g, torch.empty((n, H, S), device=DEV)))
+        wss.append(torch.zeros(gdn.gdn_decode_block_workspace_bytes(n, HK, H), dtype=torch.uint8,
+                               device=DEV))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for (t, out) in ref:
+            call(gdn.gdn_decode_block_bf16, t, out)
+        for (t, out), ws, s in zip(got, wss, streams):
+            with torch.cuda.stream(s):
+                call(gdn.gdn_decode_block_bf16_ex, t, out, ws)
+    torch.cuda.synchronize()
+    for (r, ro), (g, go), ws in zip(ref, got, wss):
+        assert torch.equal(ro, go)
+        assert torch.equal(r["state"], g["state"])
+        assert torch.equal(r["conv_state"], g["conv_state"])
+        assert int(ws.count_nonzero()) == 0
