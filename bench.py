@@ -19,7 +19,7 @@ The same line carries the other workloads of the hot path ("legs"):
               and, beside it, the one-workgroup-per-K-head layer
   decode_full the headline batch with its per-token glue launched too
               (decay gate, sigmoid, L2 norm + GQA of q and k) before the
-              recurrence
+              recurrence, and the same step as one launch (gdn_decode_step)
   decode_t4   the headline batch with the "T4" read-out (gdn_recurrence_ex)
   prefill     one bf16 layer over 1 sequence x 4096 positions through
               gdn_prefill_bf16_ex (fused conv/norm/gate front end, chunked scan
@@ -157,7 +157,8 @@ def decode_inputs(torch, gdn, inputs):
     states = [st0, st0.clone()]
     y = torch.empty((N, H, S), device="cuda")
     torch.cuda.synchronize()
-    return w, d, dict(q=q, k=k, v=raw["v"], g=g, beta=beta, y=y, states=states, glue=glue)
+    return w, d, dict(q=q, k=k, v=raw["v"], g=g, beta=beta, y=y, states=states, glue=glue,
+                      raw=raw, par=par)
 
 
 def decode_bytes(w) -> dict:
@@ -168,10 +169,15 @@ def decode_bytes(w) -> dict:
     return {"state": state, "total": state + vecs + scal}
 
 
-def run_decode(torch, gdn, inputs, steps, warmup, with_glue=False, t4=False):
+def run_decode(torch, gdn, inputs, steps, warmup, with_glue=False, t4=False, fused=False):
     w, d, t = decode_inputs(torch, gdn, inputs)
 
     def step(i):
+        if fused:   # the glue folded into the recurrence kernel: one launch
+            r, p = t["raw"], t["par"]
+            gdn.gdn_decode_step(t["states"][i % 2], r["q_raw"], r["k_raw"], r["v"], r["a"], r["b"],
+                                p["A_log"], p["dt_bias"], t["y"], w.scale, w.l2_eps)
+            return
         if with_glue:
             t["glue"]()
         if t4:
@@ -679,8 +685,11 @@ def main():
     if "decode_full" in legs:
         log("leg decode_full")
         _, _, full = run_decode(torch, gdn, inputs, K, W, with_glue=True)
+        _, _, fused = run_decode(torch, gdn, inputs, K, W, fused=True)
         out_legs["decode_full"] = {"ms_per_step": full["ms_per_step"],
-                                   "state_GBps": full["state_GBps"]}
+                                   "state_GBps": full["state_GBps"],
+                                   "fused_step_ms_per_step": fused["ms_per_step"],
+                                   "fused_step_state_GBps": fused["state_GBps"]}
         torch.cuda.empty_cache()
     if "decode_t4" in legs:
         log("leg decode_t4")

@@ -206,6 +206,31 @@ int gdn_conv1d_silu_seq_ex(const float *x, const float *w, float *conv_state, fl
                            void *stream);
 
 /*
+ * One decode step from the raw per-token inputs, in one launch: the "glue"
+ * of [CU]'s decode path (its q/k L2-norm with the grouped-query repeat,
+ * decay-gate and sigmoid kernels) folded into the recurrence:
+ *   q^ = q / max(||q||, l2_eps), k^ likewise, per K-head; V-head vh reads
+ *   K-head vh mod HK ([MLX] "GQA: tiled mapping");
+ *   g = -exp(A_log[vh]) * softplus(a + dt_bias[vh]) (softplus passed through
+ *   above 20); beta = 1 / (1 + exp(-b));
+ *   then one step of gdn_recurrence with the exact read-out.
+ * The result equals gdn_l2norm_gqa (q and k), gdn_decay_gate, gdn_sigmoid
+ * and gdn_recurrence_ex chained, bit for bit.
+ *   state   [n_seqs][n_v_heads][S][S]   (transposed layout, updated in place)
+ *   q, k    [n_seqs][n_k_heads][S]      raw (not normalised), per K-head
+ *   v, y    [n_seqs][n_v_heads][S]
+ *   a, b    [n_seqs][n_v_heads]         gate and beta inputs
+ *   A_log, dt_bias [n_v_heads]
+ * Errors: GDN_ENULL; GDN_ESIZE (a size <= 0, n_seqs < 0, n_v_heads not a
+ * multiple of n_k_heads); GDN_EUNSUPPORTED (S not in {32, 64, 128, 256});
+ * GDN_EALIGN (state, q or k not 16-byte aligned); GDN_ELAUNCH.
+ */
+int gdn_decode_step(float *state, const float *q, const float *k, const float *v,
+                    const float *a, const float *b, const float *A_log, const float *dt_bias,
+                    float *y, int n_seqs, int n_k_heads, int n_v_heads, int state_size,
+                    float scale, float l2_eps, void *stream);
+
+/*
  * Gated RMSNorm ([FM] "Gated RMSNorm"; [CU] Kernel 3): per row of head_dim
  * values, out = y / sqrt(mean(y^2) + eps) * w * silu(z), silu(z) =
  * z / (1 + exp(-z)). The weight is shared by every row (every head).

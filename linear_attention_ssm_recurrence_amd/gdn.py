@@ -58,6 +58,7 @@ def load_library():
         "gdn_conv1d_silu_seq": [P, P, P, P, I, I, I, I, P],
         "gdn_recurrence": [P, P, P, P, P, P, P, I, I, I, F, P],
         "gdn_recurrence_ex": [P, P, P, P, P, P, P, I, I, I, I, F, I, P],
+        "gdn_decode_step": [P] * 9 + [I, I, I, I, F, F, P],
         "gdn_recurrence_seq_ex": [P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, P],
         "gdn_conv1d_silu_seq_ex": [P, P, P, P, P, I, I, I, I, P],
         "gdn_recurrence_seq": [P, P, P, P, P, P, P, I, I, I, I, F, P],
@@ -254,6 +255,27 @@ def gdn_recurrence_ex(state, q, k, v, g, beta, y, scale, variant=GDN_RECUR_EXACT
     _call("gdn_recurrence_ex", _ptr(state, F32, "state"), _ptr(q, F32, "q"), _ptr(k, F32, "k"),
           _ptr(v, F32, "v"), _ptr(g, F32, "g"), _ptr(beta, F32, "beta"), _ptr(y, F32, "y"),
           N, HK, H, S, float(scale), int(variant), _stream(v, stream))
+
+
+@_typed
+def gdn_decode_step(state, q, k, v, a, b, A_log, dt_bias, y, scale, l2_eps=1e-6, stream=None):
+    """One decode step from raw inputs: state [N][H][S][S] in place; q, k
+    [N][HK][S] raw (normalised in the kernel); v, y [N][H][S]; a, b [N][H];
+    A_log, dt_bias [H]."""
+    N, H, S = v.shape
+    HK = q.shape[1]
+    _shape(state, (N, H, S, S), "state")
+    _shape(q, (N, HK, S), "q")
+    _shape(k, (N, HK, S), "k")
+    _shape(y, (N, H, S), "y")
+    _shape(a, (N, H), "a")
+    _shape(b, (N, H), "b")
+    _shape(A_log, (H,), "A_log")
+    _shape(dt_bias, (H,), "dt_bias")
+    _call("gdn_decode_step", _ptr(state, F32, "state"), _ptr(q, F32, "q"), _ptr(k, F32, "k"),
+          _ptr(v, F32, "v"), _ptr(a, F32, "a"), _ptr(b, F32, "b"), _ptr(A_log, F32, "A_log"),
+          _ptr(dt_bias, F32, "dt_bias"), _ptr(y, F32, "y"), N, HK, H, S, float(scale),
+          float(l2_eps), _stream(v, stream))
 
 
 @_typed

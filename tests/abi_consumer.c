@@ -76,6 +76,11 @@ int main(void) {
                                GDN_RECUR_T4, NULL),
          GDN_OK);
 
+  EXPECT(gdn_decode_step(f, cf, cf, cf, NULL, cf, cf, cf, f, 1, 16, 32, 128, 0.1f, 1e-6f, NULL),
+         GDN_ENULL);
+  EXPECT(gdn_decode_step(f, cf, cf, cf, cf, cf, cf, cf, f, 1, 16, 32, 96, 0.1f, 1e-6f, NULL),
+         GDN_EUNSUPPORTED);
+
   EXPECT(gdn_gated_rmsnorm(NULL, cf, cf, f, 1, 32, 1e-6f, NULL), GDN_ENULL);
   EXPECT(gdn_gated_rmsnorm(cf, cf, cf, f, 1, 0, 1e-6f, NULL), GDN_ESIZE);
 

@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_header_symbol(lib):
     names = gdn.header_symbols()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     out = os.popen(f"nm -D --defined-only {gdn.LIB_PATH}").read()
     exported = set(re.findall(r"\sT\s(gdn_\w+)", out))
     for name in names:
@@ -189,6 +189,23 @@ def test_block_validation(lib):
     assert call(state=FAKE_MIS) == gdn.GDN_EALIGN
     assert call(z=ctypes.c_void_p(0x10002)) == gdn.GDN_EALIGN
     assert call(first=NUL, state=NUL, n=0) == gdn.GDN_OK
+
+
+def test_decode_step_validation(lib):
+    f = lib.gdn_decode_step
+
+    def call(state=FAKE, q=FAKE, a=FAKE, n=2, HK=16, H=32, S=128):
+        return f(state, q, FAKE, FAKE, a, FAKE, FAKE, FAKE, FAKE, n, HK, H, S, 0.1, 1e-6, NUL)
+
+    assert call(a=NUL) == gdn.GDN_ENULL
+    assert call(state=NUL) == gdn.GDN_ENULL
+    assert call(n=-1) == gdn.GDN_ESIZE
+    assert call(HK=0) == gdn.GDN_ESIZE
+    assert call(HK=12) == gdn.GDN_ESIZE                 # 32 % 12 != 0
+    assert call(S=96) == gdn.GDN_EUNSUPPORTED
+    assert call(state=FAKE_MIS) == gdn.GDN_EALIGN
+    assert call(q=FAKE_MIS) == gdn.GDN_EALIGN
+    assert call(state=NUL, q=NUL, a=NUL, n=0) == gdn.GDN_OK
 
 
 def test_block_ex_validation(lib):
