@@ -432,6 +432,9 @@ __global__ __launch_bounds__(64 * kSplitWaves) void decode_block_split_kernel(
     }
     // Vector memory operations complete in issue order: with the IT*E/4 state
     // stores still allowed in flight, the y stores issued before them are done.
+    // The signal fences keep the compiler from moving memory operations across
+    // the wait. The immediate is gfx9's s_waitcnt encoding (vmcnt in bits 3:0,
+    // expcnt 6:4 and lgkmcnt 11:8 at their maxima, i.e. not waited on).
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt((IT * E / 4) | (7 << 4) | (15 << 8));
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
