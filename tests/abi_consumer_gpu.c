@@ -5,7 +5,11 @@
  * ragged tail) and a decode step with the T4 read-out are checked against
  * the oracle (test infrastructure, linked from oracle/liboracle_f32.so)
  * within |gpu - ref| <= 1e-5 + 1e-4 |ref|, and the scan's state against
- * chained decode launches bit for bit. Built by __graft_entry__.build(); run by
+ * chained decode launches bit for bit. The decode step from raw inputs is
+ * checked against its four stand-alone kernels, and the fused bf16 layer split
+ * over 64-row workgroups against the one-workgroup layer, bit for bit, with
+ * the split layer's workspace zeroed once by hipMemset and checked to be zero
+ * again after each call. Built by __graft_entry__.build(); run by
  * tests/test_c_gpu.py. Exit status 0 means every check passed.
  *
  * Inputs are seeded draws from splitmix64 (Steele, Lea and Flood, "Fast
@@ -124,6 +128,121 @@ static void repeat_heads(float *out, const float *in, size_t nt, int HK, int H, 
       memcpy(out + (r * H + h) * S, in + (r * HK + h % HK) * S, sizeof(float) * S);
 }
 
+/* fp32 -> bf16 bit pattern, round to nearest even (finite inputs) */
+static uint16_t to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+static void *dev_bytes(const void *host, size_t bytes) {
+  void *d = NULL;
+  HIP_OK(hipMalloc(&d, bytes));
+  if (host) HIP_OK(hipMemcpy(d, host, bytes, hipMemcpyHostToDevice));
+  return d;
+}
+
+static void all_zero(const char *what, const void *d, size_t bytes) {
+  unsigned char *h = malloc(bytes);
+  if (!h) exit(4);
+  HIP_OK(hipMemcpy(h, d, bytes, hipMemcpyDeviceToHost));
+  size_t nz = 0;
+  for (size_t i = 0; i < bytes; ++i) nz += h[i] != 0;
+  if (nz) {
+    printf("FAIL %s: %zu nonzero bytes\n", what, nz);
+    ++failures;
+  } else {
+    printf("ok   %s\n", what);
+  }
+  free(h);
+}
+
+/* The decode step from raw inputs against its stand-alone kernels, and the
+ * split fused layer against the one-workgroup layer: 3 sequences, 2 -> 4
+ * heads, S = 128, conv width 4, two chained calls. */
+static void fused_paths(hipStream_t stream) {
+  const int N = 3, HK = 2, H = 4, S = 128, K = 4, C = 2 * HK * S + H * S;
+  const float scale = 1.0f / sqrtf((float)S), eps = 1e-6f;
+  const size_t nst = (size_t)N * H * S * S, nkq = (size_t)N * HK * S, nv = (size_t)N * H * S;
+  float *st0 = malloc(nst * 4), *a = malloc((size_t)N * H * 4), *b = malloc((size_t)N * H * 4);
+  float *A_log = malloc((size_t)H * 4), *dt_bias = malloc((size_t)H * 4), *qr = malloc(nkq * 4);
+  float *kr = malloc(nkq * 4), *v = malloc(nv * 4), *conv_w = malloc((size_t)C * K * 4);
+  float *norm_w = malloc((size_t)S * 4), *cs0 = malloc((size_t)N * C * (K - 1) * 4);
+  uint16_t *qkv = malloc((size_t)N * C * 2), *z = malloc(nv * 2);
+  float *h1 = malloc(nst * 4), *h2 = malloc(nst * 4);
+  if (!st0 || !a || !b || !A_log || !dt_bias || !qr || !kr || !v || !conv_w || !norm_w || !cs0 ||
+      !qkv || !z || !h1 || !h2)
+    exit(4);
+  for (size_t i = 0; i < nst; ++i) st0[i] = 0.05f * normal();
+  for (int i = 0; i < N * H; ++i) a[i] = normal(), b[i] = normal();
+  for (int i = 0; i < H; ++i) A_log[i] = normal(), dt_bias[i] = 0.5f * normal();
+  for (size_t i = 0; i < nkq; ++i) qr[i] = normal(), kr[i] = normal();
+  for (size_t i = 0; i < nv; ++i) v[i] = normal(), z[i] = to_bf16(normal());
+  for (int i = 0; i < C * K; ++i) conv_w[i] = 0.5f * normal();
+  for (int i = 0; i < S; ++i) norm_w[i] = 1.0f + 0.1f * normal();
+  for (int i = 0; i < N * C * (K - 1); ++i) cs0[i] = normal();
+  for (int i = 0; i < N * C; ++i) qkv[i] = to_bf16(normal());
+
+  /* decode step: one launch against l2norm (q, k) + gate + sigmoid + recurrence */
+  float *d_st1 = dev_copy(st0, nst), *d_st2 = dev_copy(st0, nst);
+  float *d_qr = dev_copy(qr, nkq), *d_kr = dev_copy(kr, nkq), *d_v = dev_copy(v, nv);
+  float *d_a = dev_copy(a, (size_t)N * H), *d_b = dev_copy(b, (size_t)N * H);
+  float *d_Al = dev_copy(A_log, (size_t)H), *d_dt = dev_copy(dt_bias, (size_t)H);
+  float *d_y1 = dev_copy(NULL, nv), *d_y2 = dev_copy(NULL, nv);
+  float *d_q = dev_copy(NULL, nv), *d_k = dev_copy(NULL, nv);
+  float *d_g = dev_copy(NULL, (size_t)N * H), *d_be = dev_copy(NULL, (size_t)N * H);
+  for (int step = 0; step < 2; ++step) {
+    GDN_OK_CALL(gdn_decode_step(d_st1, d_qr, d_kr, d_v, d_a, d_b, d_Al, d_dt, d_y1, N, HK, H, S,
+                                scale, eps, stream));
+    GDN_OK_CALL(gdn_l2norm_gqa(d_qr, d_q, N, HK, H, S, eps, stream));
+    GDN_OK_CALL(gdn_l2norm_gqa(d_kr, d_k, N, HK, H, S, eps, stream));
+    GDN_OK_CALL(gdn_decay_gate(d_a, d_dt, d_Al, d_g, H, N, stream));
+    GDN_OK_CALL(gdn_sigmoid(d_b, d_be, (int64_t)N * H, stream));
+    GDN_OK_CALL(gdn_recurrence(d_st2, d_q, d_k, d_v, d_g, d_be, d_y2, N, H, S, scale, stream));
+  }
+  HIP_OK(hipStreamSynchronize(stream));
+  to_host(h1, d_y1, nv);
+  to_host(h2, d_y2, nv);
+  same_bits("decode step y = stand-alone kernels", h1, h2, nv);
+  to_host(h1, d_st1, nst);
+  to_host(h2, d_st2, nst);
+  same_bits("decode step state = stand-alone kernels", h1, h2, nst);
+
+  /* the fused bf16 layer: split over 64-row workgroups against one workgroup per K-head */
+  const size_t ws_bytes = gdn_decode_block_workspace_bytes(N, HK, H);
+  void *d_ws = dev_bytes(NULL, ws_bytes);
+  HIP_OK(hipMemset(d_ws, 0, ws_bytes));
+  uint16_t *d_qkv = dev_bytes(qkv, (size_t)N * C * 2), *d_z = dev_bytes(z, nv * 2);
+  float *d_cw = dev_copy(conv_w, (size_t)C * K), *d_nw = dev_copy(norm_w, (size_t)S);
+  float *d_cs1 = dev_copy(cs0, (size_t)N * C * (K - 1)), *d_cs2 = dev_copy(cs0, (size_t)N * C * (K - 1));
+  HIP_OK(hipMemcpy(d_st1, st0, nst * 4, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(d_st2, st0, nst * 4, hipMemcpyHostToDevice));
+  for (int step = 0; step < 2; ++step) {
+    GDN_OK_CALL(gdn_decode_block_bf16(d_qkv, d_z, d_a, d_b, d_cw, d_Al, d_dt, d_nw, d_cs1, d_st1,
+                                      d_y1, N, HK, H, S, K, scale, eps, eps, stream));
+    GDN_OK_CALL(gdn_decode_block_bf16_ex(d_qkv, d_z, d_a, d_b, d_cw, d_Al, d_dt, d_nw, d_cs2,
+                                         d_st2, d_y2, d_ws, ws_bytes, N, HK, H, S, K, scale, eps,
+                                         eps, stream));
+    HIP_OK(hipStreamSynchronize(stream));
+    all_zero("split layer workspace zero after the call", d_ws, ws_bytes);
+  }
+  to_host(h1, d_y1, nv);
+  to_host(h2, d_y2, nv);
+  same_bits("split layer out = one-workgroup layer", h1, h2, nv);
+  to_host(h1, d_st1, nst);
+  to_host(h2, d_st2, nst);
+  same_bits("split layer state = one-workgroup layer", h1, h2, nst);
+  to_host(h1, d_cs1, (size_t)N * C * (K - 1));
+  to_host(h2, d_cs2, (size_t)N * C * (K - 1));
+  same_bits("split layer conv history = one-workgroup layer", h1, h2, (size_t)N * C * (K - 1));
+
+  void *devs[] = {d_st1, d_st2, d_qr, d_kr, d_v, d_a, d_b, d_Al, d_dt, d_y1, d_y2, d_q, d_k,
+                  d_g, d_be, d_ws, d_qkv, d_z, d_cw, d_nw, d_cs1, d_cs2};
+  for (size_t i = 0; i < sizeof(devs) / sizeof(devs[0]); ++i) HIP_OK(hipFree(devs[i]));
+  free(st0), free(a), free(b), free(A_log), free(dt_bias), free(qr), free(kr), free(v);
+  free(conv_w), free(norm_w), free(cs0), free(qkv), free(z), free(h1), free(h2);
+}
+
 int main(void) {
   const int N = 3, T = 70, HK = 2, H = 4, S = 64;
   const float scale = 1.0f / sqrtf((float)S);
@@ -225,6 +344,8 @@ int main(void) {
     printf("FAIL n_v_heads %% n_k_heads != 0 was not rejected\n");
     ++failures;
   }
+
+  fused_paths(stream);
 
   HIP_OK(hipStreamDestroy(stream));
   printf("%d failures\n", failures);

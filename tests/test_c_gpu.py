@@ -2,7 +2,9 @@
 (needs an MI355X): tests/abi_consumer_gpu.c allocates with hipMalloc, runs a
 grouped-query scan and a T4 decode step through include/gdn.h, and checks
 them against the oracle within the tolerance and the scan against chained
-decode launches bit for bit. __graft_entry__.build() links it into
+decode launches bit for bit; then the one-launch decode step against its
+stand-alone kernels and the split fused layer (workspace zeroed with
+hipMemset) against the one-workgroup layer, bit for bit. __graft_entry__.build() links it into
 tests/_bin/."""
 import os
 import subprocess

@@ -83,6 +83,32 @@ def test_decode_state_past_2g_elements():
         assert_close(host(state[n, h]), st_ref[0, 0], f"decode state ({n}, {h})")
 
 
+def test_decode_step_state_past_2g_elements():
+    """The one-launch decode step from raw inputs, state past 2^31 elements."""
+    N, HK, H, S = 4097, 16, 32, 128
+    assert N * H * S * S > TWO31
+    gen = _gen(56)
+    state = _randn((N, H, S, S), gen, 0.05)
+    q, k = _randn((N, HK, S), gen), _randn((N, HK, S), gen)
+    v = _randn((N, H, S), gen)
+    a, b = _randn((N, H), gen), _randn((N, H), gen)
+    A_log, dt_bias = _randn((H,), gen), _randn((H,), gen, 0.5)
+    pairs = [(0, 0), (2048, 17), (N - 1, 2), (N - 1, H - 1)]
+    st0 = {pr: host(state[pr]) for pr in pairs}
+    y = torch.empty((N, H, S), device=DEV)
+    scale = 1 / math.sqrt(S)
+    gdn.gdn_decode_step(state, q, k, v, a, b, A_log, dt_bias, y, scale)
+    g_ref = oracle.decay_gate(host(a), host(dt_bias), host(A_log))
+    b_ref = oracle.sigmoid(host(b))
+    for n, h in pairs:
+        unit = lambda t: oracle.l2norm_gqa(host(t[n, h % HK])[None, None], 1)
+        y_ref, st_ref = oracle.recurrence(st0[(n, h)][None, None], unit(q), unit(k),
+                                          host(v[n, h])[None, None], g_ref[n, h].reshape(1, 1),
+                                          b_ref[n, h].reshape(1, 1), scale)
+        assert_close(host(y[n, h]), y_ref[0, 0], f"decode step y ({n}, {h})")
+        assert_close(host(state[n, h]), st_ref[0, 0], f"decode step state ({n}, {h})")
+
+
 @pytest.mark.parametrize("path", ["sequential", "chunked"])
 def test_scan_tokens_past_2g_elements(path):
     N, T, HK, H, S = 2, 270_000, 1, 32, 128
