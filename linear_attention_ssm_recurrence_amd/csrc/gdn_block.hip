@@ -254,7 +254,13 @@ static int launch_block_k(int K, const uint16_t* qkv, const uint16_t* z, const f
 //   * the gated norm of a V-head needs all S read-outs: each workgroup stores
 //     its rows' y to out with device-coherent stores and waits for them before
 //     it counts itself; the last of the head's workgroups reads the head's y
-//     back with device-coherent loads and writes the normalised row.
+//     back with device-coherent loads and writes the normalised row. The
+//     stores and loads are relaxed atomics of device scope (the sc1 bit on
+//     gfx950): such a store is acknowledged only once it has reached the
+//     level of the memory hierarchy that all XCDs share, and such a load
+//     reads from that level, so the hand-off holds whichever XCDs the two
+//     workgroups run on. (The numbering that puts a group on one XCD only
+//     makes the q/k re-reads hit its L2; no result depends on it.)
 // The last arriver resets its counter to zero, so the workspace is zero again
 // when the kernel ends. The arithmetic is the single-workgroup kernel's, step
 // by step and in the same order (the norm's sum of squares is row_sumsq's lane
