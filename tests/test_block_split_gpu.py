@@ -150,3 +150,24 @@ def test_split_block_empty_is_noop():
     assert gdn.load_library().gdn_decode_block_bf16_ex(
         None, None, None, None, None, None, None, None, None, None, None, None, 0,
         0, 16, 32, 128, 4, 0.1, 1e-6, 1e-6, None) == gdn.GDN_OK
+
+
+def test_split_block_degenerate_inputs():
+    """Zero activations and histories for some sequences (q and k fall to the
+    eps floor of the L2 norm, the read-out and the norm's sum to zero), gate
+    inputs at +-1e30 and on both sides of the softplus guard at 20 (decay 0 and
+    1 to fp32), and beta inputs that saturate the sigmoid: bit for bit against
+    the one-workgroup layer and within the tolerance of the oracle."""
+    rng = np.random.default_rng(500)
+    N, HK, GQ, K = 5, 3, 2, 4
+    d = _rand_layer(rng, N, HK, GQ, K)
+    H, S = HK * GQ, 128
+    zero16 = inputs.to_bf16_bits(np.zeros(1, dtype=np.float32))[0]
+    d["qkv"][1] = zero16                      # sequence 1: all conv inputs zero ...
+    d["conv_state"][1] = 0.0                  # ... and no history: q = k = v = 0
+    d["z"][2] = zero16                        # sequence 2: silu(z) = 0, out = 0
+    d["a"][3] = np.array([1e30, -1e30, 20.0, np.nextafter(np.float32(20), np.float32(21)),
+                          -80.0, 0.0], dtype=np.float32)[:H]
+    d["b"][3] = np.array([1e30, -1e30, 60.0, -60.0, 0.0, 1.0], dtype=np.float32)[:H]
+    d["state"][4] = 0.0                       # sequence 4: empty state
+    _run_chain(d, HK, 1, rng, "degenerate inputs")
