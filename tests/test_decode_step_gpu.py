@@ -33,7 +33,7 @@ def _draw(rng, N, HK, H, S):
                 b=rng.standard_normal((N, H)).astype(np.float32))
 
 
-def _check_steps(N, HK, H, S, steps, seed, zero_qk=False, l2_eps=1e-6):
+def _check_steps(N, HK, H, S, steps, seed, zero_qk=False, extreme_gate=False, l2_eps=1e-6):
     rng = np.random.default_rng(seed)
     A_log = rng.standard_normal(H).astype(np.float32)
     dt_bias = (0.5 * rng.standard_normal(H)).astype(np.float32)
@@ -46,6 +46,10 @@ def _check_steps(N, HK, H, S, steps, seed, zero_qk=False, l2_eps=1e-6):
         if zero_qk:
             x["q"][:, 0] = 0.0
             x["k"][:, -1] = 0.0
+        if extreme_gate:   # decay 0 and 1 in fp32, the softplus guard, saturated sigmoids
+            x["a"][0, :6] = [1e30, -1e30, 20.0, np.nextafter(np.float32(20), np.float32(21)),
+                             -80.0, 0.0]
+            x["b"][0, :6] = [1e30, -1e30, 60.0, -60.0, 0.0, 1.0]
         d = {key: dev(val) for key, val in x.items()}
         Al, db = dev(A_log), dev(dt_bias)
         y = torch.empty((N, H, S), device=DEV)
@@ -83,6 +87,10 @@ def test_decode_step_shapes(S, GQ):
 def test_decode_step_zero_qk():
     """q or k of a K-head all zero: the norm's eps floor gives a zero vector."""
     _check_steps(N=2, HK=4, H=8, S=128, steps=2, seed=7, zero_qk=True)
+
+
+def test_decode_step_extreme_gate_inputs():
+    _check_steps(N=2, HK=4, H=8, S=128, steps=2, seed=8, extreme_gate=True)
 
 
 def test_decode_step_256_sequences():
