@@ -19,7 +19,7 @@ from gpu_helpers import DEV, assert_close, dev, dev_bits, host, oracle_threads
 from linear_attention_ssm_recurrence_amd import gdn, inputs
 
 pytestmark = pytest.mark.gpu
-CASES = range(24)
+CASES = range(64)
 
 
 @pytest.fixture(scope="module", autouse=True)
