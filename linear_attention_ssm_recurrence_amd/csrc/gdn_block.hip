@@ -238,10 +238,10 @@ static int launch_block_k(int K, const uint16_t* qkv, const uint16_t* z, const f
 //
 // A workgroup of 8 waves owns 64 state rows of one V-head (8 rows per wave,
 // the batched decode kernel's shape): the GQ*S/64 workgroups of a (sequence,
-// K-head) group each hold a quarter or half of the state the single-workgroup
-// kernel above holds, so four of them fit a CU at once and the state streams
-// as in the plain decode (measured at 64 sequences x 16 -> 32 heads: 47.3 us
-// per layer against 50.9 us). Every workgroup convolves and L2-normalises the
+// K-head) group share out the state that the single-workgroup kernel above
+// holds in one workgroup, 32 KiB each, so four of them fit a CU at once and
+// the state streams as in the plain decode (measured at 64 sequences x
+// 16 -> 32 heads: 47.3 us per layer against 50.9 us). Every workgroup convolves and L2-normalises the
 // q and k of its K-head itself (from the same old history; 256 channels, a
 // few KB of L2 reads), and the conv channels of v are split by row, so each
 // v channel has one owner. Two steps need the whole group or the whole head,
