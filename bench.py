@@ -134,13 +134,22 @@ def host_threads() -> int:
 # legs
 # ---------------------------------------------------------------------------
 
+def dev_ssm_a(torch, gdn, A_log):
+    """The gate's per-head factor ssm_a = -exp(A_log) on the device, prepared
+    once per set of parameters by the library (gdn_ssm_a)."""
+    src = torch.from_numpy(np.ascontiguousarray(A_log, dtype=np.float32)).cuda()
+    out = torch.empty_like(src)
+    gdn.gdn_ssm_a(src, out)
+    return out
+
+
 def decode_inputs(torch, gdn, inputs):
     w = inputs.WORKLOADS[2]
     d = inputs.draw(w)
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
     N, H, HK, S = w.n_seqs, w.n_v_heads, w.n_k_heads, w.state_size
     raw = {k: dev(d[k][:, 0]) for k in ("q_raw", "k_raw", "v", "a", "b")}
-    par = {k: dev(d[k]) for k in ("A_log", "dt_bias")}
+    par = {"ssm_a": dev_ssm_a(torch, gdn, d["A_log"]), "dt_bias": dev(d["dt_bias"])}
     q = torch.empty((N, H, S), device="cuda")
     k = torch.empty((N, H, S), device="cuda")
     g = torch.empty((N, H), device="cuda")
@@ -149,7 +158,7 @@ def decode_inputs(torch, gdn, inputs):
     def glue():
         gdn.gdn_l2norm_gqa(raw["q_raw"], q, w.l2_eps)
         gdn.gdn_l2norm_gqa(raw["k_raw"], k, w.l2_eps)
-        gdn.gdn_decay_gate(raw["a"], par["dt_bias"], par["A_log"], g)
+        gdn.gdn_decay_gate(raw["a"], par["dt_bias"], par["ssm_a"], g)
         gdn.gdn_sigmoid(raw["b"], beta)
 
     glue()
@@ -176,7 +185,7 @@ def run_decode(torch, gdn, inputs, steps, warmup, with_glue=False, t4=False, fus
         if fused:   # the glue folded into the recurrence kernel: one launch
             r, p = t["raw"], t["par"]
             gdn.gdn_decode_step(t["states"][i % 2], r["q_raw"], r["k_raw"], r["v"], r["a"], r["b"],
-                                p["A_log"], p["dt_bias"], t["y"], w.scale, w.l2_eps)
+                                p["ssm_a"], p["dt_bias"], t["y"], w.scale, w.l2_eps)
             return
         if with_glue:
             t["glue"]()
@@ -218,7 +227,7 @@ def run_scan(torch, gdn, inputs, steps, warmup):
     beta = torch.empty((N, T, H), device="cuda")
     gdn.gdn_l2norm_gqa(dev(d["q_raw"]), q, w.l2_eps)
     gdn.gdn_l2norm_gqa(dev(d["k_raw"]), k, w.l2_eps)
-    gdn.gdn_decay_gate(dev(d["a"]), dev(d["dt_bias"]), dev(d["A_log"]), g)
+    gdn.gdn_decay_gate(dev(d["a"]), dev(d["dt_bias"]), dev_ssm_a(torch, gdn, d["A_log"]), g)
     gdn.gdn_sigmoid(dev(d["b"]), beta)
     v = dev(d["v"])
     st = dev(d["state"])
@@ -326,7 +335,7 @@ def run_spec(torch, gdn, inputs, steps, warmup):
     beta = torch.empty((N, T, H), device="cuda")
     gdn.gdn_l2norm_gqa(dev(d["q_raw"]), q, w.l2_eps)
     gdn.gdn_l2norm_gqa(dev(d["k_raw"]), k, w.l2_eps)
-    gdn.gdn_decay_gate(dev(d["a"]), dev(d["dt_bias"]), dev(d["A_log"]), g)
+    gdn.gdn_decay_gate(dev(d["a"]), dev(d["dt_bias"]), dev_ssm_a(torch, gdn, d["A_log"]), g)
     gdn.gdn_sigmoid(dev(d["b"]), beta)
     v, st, x, cw, cs = (dev(d[key]) for key in ("v", "state", "x", "conv_w", "conv_state"))
     y = torch.empty((N, T, H, S), device="cuda")
@@ -363,6 +372,7 @@ def run_prefill(torch, gdn, inputs, steps, warmup):
         return torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).cuda()
 
     t = {key: dev(val) for key, val in d.items()}
+    t["ssm_a"] = dev_ssm_a(torch, gdn, d["A_log"])
     out = torch.empty((N, T, H, S), device="cuda")
     ws = torch.empty(gdn.gdn_prefill_workspace_bytes(N, T, HK, H, S), dtype=torch.uint8,
                      device="cuda")
@@ -370,7 +380,7 @@ def run_prefill(torch, gdn, inputs, steps, warmup):
     torch.cuda.synchronize()
 
     def step(scan):
-        gdn.gdn_prefill_bf16(t["qkv"], t["z"], t["a"], t["b"], t["conv_w"], t["A_log"],
+        gdn.gdn_prefill_bf16(t["qkv"], t["z"], t["a"], t["b"], t["conv_w"], t["ssm_a"],
                              t["dt_bias"], t["norm_w"], t["conv_state"], t["state"], out, ws, HK,
                              scale, scan=scan)
 
@@ -402,7 +412,7 @@ def run_single(torch, gdn, inputs, steps, warmup):
     beta = torch.empty((1, H), device="cuda")
     gdn.gdn_l2norm_gqa(dev(d["q_raw"][:, 0]), q, w.l2_eps)
     gdn.gdn_l2norm_gqa(dev(d["k_raw"][:, 0]), k, w.l2_eps)
-    gdn.gdn_decay_gate(dev(d["a"][:, 0]), dev(d["dt_bias"]), dev(d["A_log"]), g)
+    gdn.gdn_decay_gate(dev(d["a"][:, 0]), dev(d["dt_bias"]), dev_ssm_a(torch, gdn, d["A_log"]), g)
     gdn.gdn_sigmoid(dev(d["b"][:, 0]), beta)
     v, st, z = dev(d["v"][:, 0]), dev(d["state"]), dev(d["z"][:, 0])
     x, cw, cs, nw = dev(d["x"][:, 0]), dev(d["conv_w"]), dev(d["conv_state"]), dev(d["norm_w"])
@@ -414,6 +424,7 @@ def run_single(torch, gdn, inputs, steps, warmup):
     lb = inputs.draw_block_layer(0, wb, n_seqs=1)
     bits = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
     b_in = {key: (bits(val) if val.dtype == np.uint16 else dev(val)) for key, val in lb.items()}
+    b_in["ssm_a"] = dev_ssm_a(torch, gdn, lb["A_log"])
     b_out = torch.empty((1, H, S), device="cuda")
     flush = torch.empty(256 * 1024 * 1024, device="cuda")    # 1 GiB > the 256 MB Infinity Cache
     torch.cuda.synchronize()
@@ -425,7 +436,7 @@ def run_single(torch, gdn, inputs, steps, warmup):
 
     def fused():
         gdn.gdn_decode_block_bf16(b_in["qkv"], b_in["z"], b_in["a"], b_in["b"], b_in["conv_w"],
-                                  b_in["A_log"], b_in["dt_bias"], b_in["norm_w"],
+                                  b_in["ssm_a"], b_in["dt_bias"], b_in["norm_w"],
                                   b_in["conv_state"], b_in["state"], b_out, HK, wb.scale,
                                   wb.l2_eps, wb.eps)
 
@@ -434,7 +445,7 @@ def run_single(torch, gdn, inputs, steps, warmup):
 
     def fused_split():
         gdn.gdn_decode_block_bf16_ex(b_in["qkv"], b_in["z"], b_in["a"], b_in["b"],
-                                     b_in["conv_w"], b_in["A_log"], b_in["dt_bias"],
+                                     b_in["conv_w"], b_in["ssm_a"], b_in["dt_bias"],
                                      b_in["norm_w"], b_in["conv_state"], b_in["state"], b_out,
                                      ws1, HK, wb.scale, wb.l2_eps, wb.eps)
 
@@ -493,6 +504,18 @@ def run_single(torch, gdn, inputs, steps, warmup):
     return r
 
 
+def probe_fma_fn():
+    """gdn_probe_fma from the benchmark's own probe library (built beside
+    libgdn.so, not part of it)."""
+    import ctypes
+    path = os.path.join(ROOT, "linear_attention_ssm_recurrence_amd", "libgdn_probe.so")
+    fn = ctypes.CDLL(path).gdn_probe_fma
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_float,
+                   ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    return fn
+
+
 def run_machine(torch, gdn, steps):
     """What this GPU achieves: a plain device copy and the fp32 FMA issue rate."""
     src = torch.ones(256 * 1024 * 1024, device="cuda")       # 1 GiB
@@ -507,10 +530,18 @@ def run_machine(torch, gdn, steps):
     del src, dst
     blocks, iters = 256 * 8, 4096
     out = torch.empty(blocks * 256, device="cuda")
-    gdn.gdn_probe_fma(out, iters)
+    probe = probe_fma_fn()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def fma():
+        rc = probe(out.data_ptr(), blocks, iters, 0.999, 1e-3, stream)
+        if rc != 0:
+            raise RuntimeError(f"gdn_probe_fma returned {rc}")
+
+    fma()
     with Timer(torch) as tf:
         for _ in range(reps):
-            gdn.gdn_probe_fma(out, iters)
+            fma()
     flops = blocks * 256 * iters * 32 * reps
     return {"copy_1GiB_GBps": copy_gbps, "copy_frac_hbm_peak": copy_gbps / HBM_PEAK_GBS,
             "fma_chain_TFLOPs": flops / (tf.event_ms * 1e-3) / 1e12,
@@ -543,6 +574,7 @@ def run_block(torch, gdn, inputs, steps, warmup):
                     arr = arr.view(np.int16)
                 dv[key] = torch.from_numpy(arr).cuda()
             dv["out"] = torch.empty((N, H, S), device="cuda")
+            dv["ssm_a"] = dev_ssm_a(torch, gdn, d["A_log"])
             layers.append(dv)
         log(f"block: {len(layers)}/{Lyr} layers resident")
     torch.cuda.synchronize()
@@ -553,12 +585,12 @@ def run_block(torch, gdn, inputs, steps, warmup):
     def step_split():
         for t in layers:
             gdn.gdn_decode_block_bf16_ex(t["qkv"], t["z"], t["a"], t["b"], t["conv_w"],
-                                         t["A_log"], t["dt_bias"], t["norm_w"], t["conv_state"],
+                                         t["ssm_a"], t["dt_bias"], t["norm_w"], t["conv_state"],
                                          t["state"], t["out"], ws, HK, w.scale, w.l2_eps, w.eps)
 
     def step_one():
         for t in layers:
-            gdn.gdn_decode_block_bf16(t["qkv"], t["z"], t["a"], t["b"], t["conv_w"], t["A_log"],
+            gdn.gdn_decode_block_bf16(t["qkv"], t["z"], t["a"], t["b"], t["conv_w"], t["ssm_a"],
                                       t["dt_bias"], t["norm_w"], t["conv_state"], t["state"],
                                       t["out"], HK, w.scale, w.l2_eps, w.eps)
 

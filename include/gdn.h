@@ -17,7 +17,13 @@
  *   - Arrays are dense and row-major (last index fastest), fp32 unless a
  *     parameter says bf16; bf16 values are passed as their 16-bit patterns.
  *   - Arguments are validated before anything is enqueued: on any non-zero
- *     return nothing was launched and no memory was touched. Shape arguments
+ *     return other than GDN_ELAUNCH nothing was launched and no memory was
+ *     touched. GDN_ELAUNCH is the status of the call's own launch (the HIP
+ *     runtime's return value for it): an error left pending on the calling
+ *     thread by an earlier call is neither reported nor cleared. Of the entry
+ *     points that enqueue several kernels (the chunked scan, the prefill), one
+ *     that returns GDN_ELAUNCH may have enqueued the kernels before the one
+ *     that was rejected. Shape arguments
  *     (heads, state_size, head_dim, conv_dim, conv_kernel) must be positive.
  *     A count argument (n_seqs, n_tokens, rows, n, n_rows) of 0 is an empty
  *     input: the call returns GDN_OK and launches nothing, and its pointers
@@ -61,15 +67,27 @@ const char *gdn_strerror(int code);
 int gdn_abi_version(void);
 
 /*
+ * The gate's per-head factor ssm_a = -exp(A_log) ([CU] fc_ssm_decay_gate,
+ * whose comment has it prepared once on the host; [FM] "Decay gate" takes it
+ * as its `a` buffer). Every entry point that forms the gate takes ssm_a, as
+ * both pages do; a caller that holds the model's A_log prepares ssm_a once
+ * per set of parameters with this call.
+ *   A_log, ssm_a [n_heads]   (ssm_a may equal A_log: in place)
+ * Errors: GDN_ENULL, GDN_ESIZE (n_heads < 0), GDN_ELAUNCH.
+ */
+int gdn_ssm_a(const float *A_log, float *ssm_a, int n_heads, void *stream);
+
+/*
  * Decay gate ([CU] fc_ssm_decay_gate / fc_ssm_decay_gate_nx; [FM] "Decay
- * gate"):  g[r][h] = -exp(A_log[h]) * softplus(a[r][h] + dt_bias[h]),
- * softplus(u) = u when u > 20, else log1p(exp(u)). g <= 0, so the decay
- * exp(g) of the recurrence lies in (0, 1].
- *   a, g          [rows][n_heads]
- *   dt_bias, A_log [n_heads]
+ * gate"):  g[r][h] = ssm_a[h] * softplus(a[r][h] + dt_bias[h]),
+ * softplus(u) = u when u > 20, else log1p(exp(u)). With ssm_a = -exp(A_log)
+ * <= 0 (gdn_ssm_a), g <= 0, so the decay exp(g) of the recurrence lies in
+ * (0, 1].
+ *   a, g           [rows][n_heads]
+ *   dt_bias, ssm_a [n_heads]
  * Errors: GDN_ENULL, GDN_ESIZE (n_heads <= 0, rows < 0), GDN_ELAUNCH.
  */
-int gdn_decay_gate(const float *a, const float *dt_bias, const float *A_log, float *g,
+int gdn_decay_gate(const float *a, const float *dt_bias, const float *ssm_a, float *g,
                    int n_heads, int64_t rows, void *stream);
 
 /*
@@ -211,7 +229,7 @@ int gdn_conv1d_silu_seq_ex(const float *x, const float *w, float *conv_state, fl
  * decay-gate and sigmoid kernels) folded into the recurrence:
  *   q^ = q / max(||q||, l2_eps), k^ likewise, per K-head; V-head vh reads
  *   K-head vh mod HK ([MLX] "GQA: tiled mapping");
- *   g = -exp(A_log[vh]) * softplus(a + dt_bias[vh]) (softplus passed through
+ *   g = ssm_a[vh] * softplus(a + dt_bias[vh]) (softplus passed through
  *   above 20); beta = 1 / (1 + exp(-b));
  *   then one step of gdn_recurrence with the exact read-out.
  * The result equals gdn_l2norm_gqa (q and k), gdn_decay_gate, gdn_sigmoid
@@ -220,13 +238,13 @@ int gdn_conv1d_silu_seq_ex(const float *x, const float *w, float *conv_state, fl
  *   q, k    [n_seqs][n_k_heads][S]      raw (not normalised), per K-head
  *   v, y    [n_seqs][n_v_heads][S]
  *   a, b    [n_seqs][n_v_heads]         gate and beta inputs
- *   A_log, dt_bias [n_v_heads]
+ *   ssm_a, dt_bias [n_v_heads]
  * Errors: GDN_ENULL; GDN_ESIZE (a size <= 0, n_seqs < 0, n_v_heads not a
  * multiple of n_k_heads); GDN_EUNSUPPORTED (S not in {32, 64, 128, 256});
  * GDN_EALIGN (state, q or k not 16-byte aligned); GDN_ELAUNCH.
  */
 int gdn_decode_step(float *state, const float *q, const float *k, const float *v,
-                    const float *a, const float *b, const float *A_log, const float *dt_bias,
+                    const float *a, const float *b, const float *ssm_a, const float *dt_bias,
                     float *y, int n_seqs, int n_k_heads, int n_v_heads, int state_size,
                     float scale, float l2_eps, void *stream);
 
@@ -250,14 +268,14 @@ int gdn_gated_rmsnorm(const float *y, const float *w, const float *z, float *out
  *   2. split the conv output as [q: HK*S | k: HK*S | v: H*S];
  *   3. L2-normalise q and k per K-head (l2_eps); V-head vh reads K-head
  *      vh mod HK;
- *   4. beta = sigmoid(b[n][vh]); g = -exp(A_log[vh]) *
- *      softplus(a[n][vh] + dt_bias[vh]);
+ *   4. beta = sigmoid(b[n][vh]); g = ssm_a[vh] *
+ *      softplus(a[n][vh] + dt_bias[vh]), ssm_a = -exp(A_log) (gdn_ssm_a);
  *   5. one recurrence step of state[n][vh], y = scale * (row . q);
  *   6. out[n][vh] = gated RMSNorm(y[vh], norm_w, widened z[n][vh], eps).
  *   qkv        [n_seqs][C] bf16, C = 2*HK*S + H*S
  *   z          [n_seqs][n_v_heads][S] bf16
  *   a, b       [n_seqs][n_v_heads]
- *   conv_w     [C][conv_kernel];  A_log, dt_bias [n_v_heads];  norm_w [S]
+ *   conv_w     [C][conv_kernel];  ssm_a, dt_bias [n_v_heads];  norm_w [S]
  *   conv_state [n_seqs][C][conv_kernel - 1]   (updated in place)
  *   state      [n_seqs][n_v_heads][S][S]      (updated in place)
  *   out        [n_seqs][n_v_heads][S]
@@ -266,7 +284,7 @@ int gdn_gated_rmsnorm(const float *y, const float *w, const float *z, float *out
  * GDN_EALIGN (state, norm_w or out not 16-byte aligned); GDN_ELAUNCH.
  */
 int gdn_decode_block_bf16(const uint16_t *qkv, const uint16_t *z, const float *a,
-                          const float *b, const float *conv_w, const float *A_log,
+                          const float *b, const float *conv_w, const float *ssm_a,
                           const float *dt_bias, const float *norm_w, float *conv_state,
                           float *state, float *out, int n_seqs, int n_k_heads, int n_v_heads,
                           int state_size, int conv_kernel, float scale, float l2_eps, float eps,
@@ -297,7 +315,7 @@ size_t gdn_decode_block_workspace_bytes(int n_seqs, int n_k_heads, int n_v_heads
  * GDN_ESIZE (workspace too small), GDN_EALIGN (workspace not 4-byte aligned).
  */
 int gdn_decode_block_bf16_ex(const uint16_t *qkv, const uint16_t *z, const float *a,
-                             const float *b, const float *conv_w, const float *A_log,
+                             const float *b, const float *conv_w, const float *ssm_a,
                              const float *dt_bias, const float *norm_w, float *conv_state,
                              float *state, float *out, void *workspace, size_t workspace_bytes,
                              int n_seqs, int n_k_heads, int n_v_heads, int state_size,
@@ -318,7 +336,7 @@ size_t gdn_prefill_workspace_bytes(int n_seqs, int n_tokens, int n_k_heads, int 
  * pass-through, decay_gate_nx, recurrence_seq; then the gated norm).
  *   1. conv1d + SiLU over the positions of the widened qkv (rolls
  *      conv_state), split [q | k | v], q and k L2-normalised per K-head
- *      (l2_eps), g = -exp(A_log)*softplus(a + dt_bias), beta = sigmoid(b);
+ *      (l2_eps), g = ssm_a*softplus(a + dt_bias), beta = sigmoid(b);
  *   2. the sequential scan, V-head vh reading K-head vh mod HK, y = scale *
  *      (row . q);
  *   3. out = gated RMSNorm(y, norm_w, widened z, eps).
@@ -326,7 +344,7 @@ size_t gdn_prefill_workspace_bytes(int n_seqs, int n_tokens, int n_k_heads, int 
  *   qkv        [n_seqs][n_tokens][C] bf16, C = 2*HK*S + H*S (8-byte aligned)
  *   z          [n_seqs][n_tokens][n_v_heads][S] bf16 (8-byte aligned)
  *   a, b       [n_seqs][n_tokens][n_v_heads]
- *   conv_w [C][conv_kernel]; A_log, dt_bias [n_v_heads]; norm_w [S]
+ *   conv_w [C][conv_kernel]; ssm_a, dt_bias [n_v_heads]; norm_w [S]
  *   conv_state [n_seqs][C][conv_kernel-1], state [n_seqs][n_v_heads][S][S]
  *              (both updated in place)
  *   out        [n_seqs][n_tokens][n_v_heads][S]
@@ -338,7 +356,7 @@ size_t gdn_prefill_workspace_bytes(int n_seqs, int n_tokens, int n_k_heads, int 
  * 2..4); GDN_EALIGN; GDN_ELAUNCH.
  */
 int gdn_prefill_bf16(const uint16_t *qkv, const uint16_t *z, const float *a, const float *b,
-                     const float *conv_w, const float *A_log, const float *dt_bias,
+                     const float *conv_w, const float *ssm_a, const float *dt_bias,
                      const float *norm_w, float *conv_state, float *state, float *out,
                      void *workspace, size_t workspace_bytes, int n_seqs, int n_tokens,
                      int n_k_heads, int n_v_heads, int state_size, int conv_kernel, float scale,
@@ -385,7 +403,7 @@ int gdn_recurrence_seq_chunked(float *state, const float *q, const float *k, con
  * Errors: as gdn_prefill_bf16, and GDN_EUNSUPPORTED for an unknown scan.
  */
 int gdn_prefill_bf16_ex(const uint16_t *qkv, const uint16_t *z, const float *a, const float *b,
-                        const float *conv_w, const float *A_log, const float *dt_bias,
+                        const float *conv_w, const float *ssm_a, const float *dt_bias,
                         const float *norm_w, float *conv_state, float *state, float *out,
                         void *workspace, size_t workspace_bytes, int n_seqs, int n_tokens,
                         int n_k_heads, int n_v_heads, int state_size, int conv_kernel, float scale,

@@ -38,7 +38,7 @@ template <int GQ, int K>
 __global__ __launch_bounds__(64 * kBlockWaves) void decode_block_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ z, const float* __restrict__ a,
     const float* __restrict__ b, const float* __restrict__ conv_w,
-    const float* __restrict__ A_log, const float* __restrict__ dt_bias,
+    const float* __restrict__ ssm_a, const float* __restrict__ dt_bias,
     const float* __restrict__ norm_w, float* __restrict__ conv_state, float* __restrict__ state,
     float* __restrict__ out, int n_k_heads, float scale, float l2_eps, float eps) {
   constexpr int S = kBlockS;
@@ -86,12 +86,12 @@ __global__ __launch_bounds__(64 * kBlockWaves) void decode_block_kernel(
     }
   }
   const bool gate_lane = (wv == 2 && lane < GQ);
-  float ga = 0.0f, gdt = 0.0f, gal = 0.0f, gb = 0.0f;
+  float ga = 0.0f, gdt = 0.0f, gsa = 0.0f, gb = 0.0f;
   if (gate_lane) {
     const int h = kh + lane * n_k_heads;
     ga = a[n * n_v_heads + h];
     gdt = dt_bias[h];
-    gal = A_log[h];
+    gsa = ssm_a[h];
     gb = b[n * n_v_heads + h];
   }
 
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(64 * kBlockWaves) void decode_block_kernel(
       store4(x + 4 * m, v);
     }
   } else if (gate_lane) {
-    const float gv = decay_gate(ga, gdt, gal);
+    const float gv = decay_gate(ga, gdt, gsa);
     gate_d[lane] = expf(gv);
     gate_b[lane] = sigmoid(gb);
   }
@@ -207,27 +207,26 @@ __global__ __launch_bounds__(64 * kBlockWaves) void decode_block_kernel(
 
 template <int GQ, int K>
 static int launch_block(const uint16_t* qkv, const uint16_t* z, const float* a, const float* b,
-                        const float* conv_w, const float* A_log, const float* dt_bias,
+                        const float* conv_w, const float* ssm_a, const float* dt_bias,
                         const float* norm_w, float* conv_state, float* state, float* out,
                         int n_seqs, int n_k_heads, float scale, float l2_eps, float eps,
                         hipStream_t s) {
   const int64_t blocks = (int64_t)n_seqs * n_k_heads;
-  hipLaunchKernelGGL((decode_block_kernel<GQ, K>), dim3((unsigned)blocks), dim3(64 * kBlockWaves),
-                     0, s, qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out,
-                     n_k_heads, scale, l2_eps, eps);
-  return launch_status();
+  return launch(decode_block_kernel<GQ, K>, dim3((unsigned)blocks), dim3(64 * kBlockWaves),
+                0, s, qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state, state, out,
+                n_k_heads, scale, l2_eps, eps);
 }
 
 template <int GQ>
 static int launch_block_k(int K, const uint16_t* qkv, const uint16_t* z, const float* a,
-                          const float* b, const float* conv_w, const float* A_log,
+                          const float* b, const float* conv_w, const float* ssm_a,
                           const float* dt_bias, const float* norm_w, float* conv_state,
                           float* state, float* out, int n_seqs, int n_k_heads, float scale,
                           float l2_eps, float eps, hipStream_t s) {
   switch (K) {
-    case 2: return launch_block<GQ, 2>(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, n_seqs, n_k_heads, scale, l2_eps, eps, s);
-    case 3: return launch_block<GQ, 3>(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, n_seqs, n_k_heads, scale, l2_eps, eps, s);
-    case 4: return launch_block<GQ, 4>(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, n_seqs, n_k_heads, scale, l2_eps, eps, s);
+    case 2: return launch_block<GQ, 2>(qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state, state, out, n_seqs, n_k_heads, scale, l2_eps, eps, s);
+    case 3: return launch_block<GQ, 3>(qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state, state, out, n_seqs, n_k_heads, scale, l2_eps, eps, s);
+    case 4: return launch_block<GQ, 4>(qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state, state, out, n_seqs, n_k_heads, scale, l2_eps, eps, s);
   }
   return GDN_EUNSUPPORTED;
 }
@@ -273,7 +272,7 @@ template <int GQ, int K>
 __global__ __launch_bounds__(64 * kSplitWaves) void decode_block_split_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ z, const float* __restrict__ a,
     const float* __restrict__ b, const float* __restrict__ conv_w,
-    const float* __restrict__ A_log, const float* __restrict__ dt_bias,
+    const float* __restrict__ ssm_a, const float* __restrict__ dt_bias,
     const float* __restrict__ norm_w, float* __restrict__ conv_state, float* __restrict__ state,
     float* __restrict__ out, unsigned* __restrict__ counters, int64_t n_groups, int n_k_heads,
     float scale, float l2_eps, float eps) {
@@ -333,11 +332,11 @@ __global__ __launch_bounds__(64 * kSplitWaves) void decode_block_split_kernel(
     xv = bf16_to_float(qkv[n * C + c]);
   }
   const bool gate_lane = (wv == 5 && lane == 0);
-  float ga = 0.0f, gdt = 0.0f, gal = 0.0f, gb = 0.0f;
+  float ga = 0.0f, gdt = 0.0f, gsa = 0.0f, gb = 0.0f;
   if (gate_lane) {
     ga = a[pair];
     gdt = dt_bias[vh];
-    gal = A_log[vh];
+    gsa = ssm_a[vh];
     gb = b[pair];
   }
   static_assert(S / 4 <= 64, "one float4 group of the norm row per lane");
@@ -391,7 +390,7 @@ __global__ __launch_bounds__(64 * kSplitWaves) void decode_block_split_kernel(
       store4(x + 4 * m, v);
     }
   } else if (gate_lane) {
-    const float gv = decay_gate(ga, gdt, gal);
+    const float gv = decay_gate(ga, gdt, gsa);
     gate_d = expf(gv);
     gate_b = sigmoid(gb);
   }
@@ -495,28 +494,27 @@ __global__ __launch_bounds__(64 * kSplitWaves) void decode_block_split_kernel(
 
 template <int GQ, int K>
 static int launch_block_split(const uint16_t* qkv, const uint16_t* z, const float* a,
-                              const float* b, const float* conv_w, const float* A_log,
+                              const float* b, const float* conv_w, const float* ssm_a,
                               const float* dt_bias, const float* norm_w, float* conv_state,
                               float* state, float* out, unsigned* counters, int64_t groups,
                               int n_k_heads, float scale, float l2_eps, float eps, hipStream_t s) {
   constexpr int P = GQ * (kBlockS / kSplitRows);
   const int64_t blocks = ((groups + kXcds - 1) / kXcds) * kXcds * P;
-  hipLaunchKernelGGL((decode_block_split_kernel<GQ, K>), dim3((unsigned)blocks),
-                     dim3(64 * kSplitWaves), 0, s, qkv, z, a, b, conv_w, A_log, dt_bias, norm_w,
-                     conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps);
-  return launch_status();
+  return launch(decode_block_split_kernel<GQ, K>, dim3((unsigned)blocks),
+                dim3(64 * kSplitWaves), 0, s, qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w,
+                conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps);
 }
 
 template <int GQ>
 static int launch_block_split_k(int K, const uint16_t* qkv, const uint16_t* z, const float* a,
-                                const float* b, const float* conv_w, const float* A_log,
+                                const float* b, const float* conv_w, const float* ssm_a,
                                 const float* dt_bias, const float* norm_w, float* conv_state,
                                 float* state, float* out, unsigned* counters, int64_t groups,
                                 int n_k_heads, float scale, float l2_eps, float eps, hipStream_t s) {
   switch (K) {
-    case 2: return launch_block_split<GQ, 2>(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps, s);
-    case 3: return launch_block_split<GQ, 3>(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps, s);
-    case 4: return launch_block_split<GQ, 4>(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps, s);
+    case 2: return launch_block_split<GQ, 2>(qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps, s);
+    case 3: return launch_block_split<GQ, 3>(qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps, s);
+    case 4: return launch_block_split<GQ, 4>(qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps, s);
   }
   return GDN_EUNSUPPORTED;
 }
@@ -526,7 +524,7 @@ static int launch_block_split_k(int K, const uint16_t* qkv, const uint16_t* z, c
 using namespace gdn;
 
 extern "C" int gdn_decode_block_bf16(const uint16_t* qkv, const uint16_t* z, const float* a,
-                                     const float* b, const float* conv_w, const float* A_log,
+                                     const float* b, const float* conv_w, const float* ssm_a,
                                      const float* dt_bias, const float* norm_w,
                                      float* conv_state, float* state, float* out, int n_seqs,
                                      int n_k_heads, int n_v_heads, int state_size,
@@ -539,7 +537,7 @@ extern "C" int gdn_decode_block_bf16(const uint16_t* qkv, const uint16_t* z, con
   if (state_size != kBlockS || !(gq == 1 || gq == 2 || gq == 4)) return GDN_EUNSUPPORTED;
   if (conv_kernel < 2 || conv_kernel > 4) return GDN_EUNSUPPORTED;
   if (n_seqs == 0) return GDN_OK;
-  if (!qkv || !z || !a || !b || !conv_w || !A_log || !dt_bias || !norm_w || !conv_state ||
+  if (!qkv || !z || !a || !b || !conv_w || !ssm_a || !dt_bias || !norm_w || !conv_state ||
       !state || !out)
     return GDN_ENULL;
   int64_t pairs, st;
@@ -550,9 +548,9 @@ extern "C" int gdn_decode_block_bf16(const uint16_t* qkv, const uint16_t* z, con
   if ((reinterpret_cast<uintptr_t>(z) & 7u) != 0) return GDN_EALIGN;
   hipStream_t s = as_stream(stream);
   switch (gq) {
-    case 1: return launch_block_k<1>(conv_kernel, qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, n_seqs, n_k_heads, scale, l2_eps, eps, s);
-    case 2: return launch_block_k<2>(conv_kernel, qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, n_seqs, n_k_heads, scale, l2_eps, eps, s);
-    case 4: return launch_block_k<4>(conv_kernel, qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, n_seqs, n_k_heads, scale, l2_eps, eps, s);
+    case 1: return launch_block_k<1>(conv_kernel, qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state, state, out, n_seqs, n_k_heads, scale, l2_eps, eps, s);
+    case 2: return launch_block_k<2>(conv_kernel, qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state, state, out, n_seqs, n_k_heads, scale, l2_eps, eps, s);
+    case 4: return launch_block_k<4>(conv_kernel, qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state, state, out, n_seqs, n_k_heads, scale, l2_eps, eps, s);
   }
   return GDN_EUNSUPPORTED;
 }
@@ -574,41 +572,67 @@ extern "C" size_t gdn_decode_block_workspace_bytes(int n_seqs, int n_k_heads, in
   return (size_t)count * sizeof(unsigned);
 }
 
-extern "C" int gdn_decode_block_bf16_ex(const uint16_t* qkv, const uint16_t* z, const float* a,
-                                        const float* b, const float* conv_w, const float* A_log,
-                                        const float* dt_bias, const float* norm_w,
-                                        float* conv_state, float* state, float* out,
-                                        void* workspace, size_t workspace_bytes, int n_seqs,
-                                        int n_k_heads, int n_v_heads, int state_size,
-                                        int conv_kernel, float scale, float l2_eps, float eps,
-                                        void* stream) {
+// Argument checks of the split layer (all but the workspace's), shared by the
+// workspace and the allocation-free entry points.
+static int check_block_split(const uint16_t* qkv, const uint16_t* z, const float* a,
+                             const float* b, const float* conv_w, const float* ssm_a,
+                             const float* dt_bias, const float* norm_w, const float* conv_state,
+                             const float* state, const float* out, int n_seqs, int n_k_heads,
+                             int n_v_heads, int state_size, int conv_kernel, int64_t* counters) {
   if (n_seqs < 0 || n_k_heads <= 0 || n_v_heads <= 0 || state_size <= 0 || conv_kernel <= 0)
     return GDN_ESIZE;
   if (n_v_heads % n_k_heads != 0) return GDN_ESIZE;
   const int gq = n_v_heads / n_k_heads;
   if (state_size != kBlockS || !(gq == 1 || gq == 2 || gq == 4)) return GDN_EUNSUPPORTED;
   if (conv_kernel < 2 || conv_kernel > 4) return GDN_EUNSUPPORTED;
-  if (n_seqs == 0) return GDN_OK;
-  if (!qkv || !z || !a || !b || !conv_w || !A_log || !dt_bias || !norm_w || !conv_state ||
-      !state || !out || !workspace)
+  if (n_seqs == 0) return kNothingToDo;
+  if (!qkv || !z || !a || !b || !conv_w || !ssm_a || !dt_bias || !norm_w || !conv_state ||
+      !state || !out)
     return GDN_ENULL;
-  int64_t pairs, st, count;
+  int64_t pairs, st;
   if (!mul_ok(n_seqs, n_v_heads, &pairs) || !mul_ok(pairs, (int64_t)state_size * state_size, &st))
     return GDN_ESIZE;
-  if (!block_counters(n_seqs, n_k_heads, n_v_heads, &count)) return GDN_ESIZE;
-  if (workspace_bytes < (size_t)count * sizeof(unsigned)) return GDN_ESIZE;
+  if (!block_counters(n_seqs, n_k_heads, n_v_heads, counters)) return GDN_ESIZE;
   const int64_t groups = (int64_t)n_seqs * n_k_heads;
   const int64_t blocks = ((groups + kXcds - 1) / kXcds) * kXcds * gq * (kBlockS / kSplitRows);
   if (blocks >= (int64_t(1) << 31)) return GDN_ESIZE;
   if (!aligned16(state) || !aligned16(norm_w) || !aligned16(out)) return GDN_EALIGN;
   if ((reinterpret_cast<uintptr_t>(z) & 7u) != 0) return GDN_EALIGN;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return GDN_EALIGN;
-  hipStream_t s = as_stream(stream);
-  unsigned* counters = static_cast<unsigned*>(workspace);
-  switch (gq) {
-    case 1: return launch_block_split_k<1>(conv_kernel, qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps, s);
-    case 2: return launch_block_split_k<2>(conv_kernel, qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps, s);
-    case 4: return launch_block_split_k<4>(conv_kernel, qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps, s);
+  return GDN_OK;
+}
+
+static int dispatch_block_split(const uint16_t* qkv, const uint16_t* z, const float* a,
+                                const float* b, const float* conv_w, const float* ssm_a,
+                                const float* dt_bias, const float* norm_w, float* conv_state,
+                                float* state, float* out, unsigned* counters, int n_seqs,
+                                int n_k_heads, int n_v_heads, int conv_kernel, float scale,
+                                float l2_eps, float eps, hipStream_t s) {
+  const int64_t groups = (int64_t)n_seqs * n_k_heads;
+  switch (n_v_heads / n_k_heads) {
+    case 1: return launch_block_split_k<1>(conv_kernel, qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps, s);
+    case 2: return launch_block_split_k<2>(conv_kernel, qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps, s);
+    case 4: return launch_block_split_k<4>(conv_kernel, qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state, state, out, counters, groups, n_k_heads, scale, l2_eps, eps, s);
   }
   return GDN_EUNSUPPORTED;
+}
+
+extern "C" int gdn_decode_block_bf16_ex(const uint16_t* qkv, const uint16_t* z, const float* a,
+                                        const float* b, const float* conv_w, const float* ssm_a,
+                                        const float* dt_bias, const float* norm_w,
+                                        float* conv_state, float* state, float* out,
+                                        void* workspace, size_t workspace_bytes, int n_seqs,
+                                        int n_k_heads, int n_v_heads, int state_size,
+                                        int conv_kernel, float scale, float l2_eps, float eps,
+                                        void* stream) {
+  int64_t count = 0;
+  const int rc = check_block_split(qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state,
+                                   state, out, n_seqs, n_k_heads, n_v_heads, state_size,
+                                   conv_kernel, &count);
+  if (rc != GDN_OK) return finish_check(rc);
+  if (!workspace) return GDN_ENULL;
+  if (workspace_bytes < (size_t)count * sizeof(unsigned)) return GDN_ESIZE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return GDN_EALIGN;
+  return dispatch_block_split(qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state, state,
+                              out, static_cast<unsigned*>(workspace), n_seqs, n_k_heads,
+                              n_v_heads, conv_kernel, scale, l2_eps, eps, as_stream(stream));
 }

@@ -610,6 +610,21 @@ void chunk_scan_kernel(float* __restrict__ state, const float* __restrict__ q,
 
 using namespace gdn;
 
+namespace gdn {
+
+// Grid limits of the two chunked kernels (the preparation's blocks never
+// outnumber the (sequence, V-head, chunk) units), for shapes that are
+// otherwise valid; also used by the prefill before it launches anything.
+int chunked_size_check(int64_t n_seqs, int64_t n_tokens, int n_v_heads) {
+  const int64_t n_chunks = (n_tokens + kChC - 1) / kChC;
+  const int64_t units = n_seqs * n_v_heads * n_chunks;
+  const int64_t scan_blocks = n_seqs * n_v_heads * (kChS / kChR);
+  if (units >= (int64_t(1) << 31) || scan_blocks >= (int64_t(1) << 31)) return GDN_ESIZE;
+  return GDN_OK;
+}
+
+}  // namespace gdn
+
 extern "C" size_t gdn_chunked_workspace_bytes(int n_seqs, int n_tokens, int n_v_heads,
                                               int state_size) {
   if (n_seqs < 0 || n_tokens < 0 || n_v_heads <= 0 || state_size != kChS) return 0;
@@ -633,8 +648,8 @@ extern "C" int gdn_recurrence_seq_chunked(float* state, const float* q, const fl
   if (!aligned16(state) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y) ||
       !aligned16(workspace))
     return GDN_EALIGN;
+  if (chunked_size_check(n_seqs, n_tokens, n_v_heads) != GDN_OK) return GDN_ESIZE;
   const int n_chunks = (n_tokens + kChC - 1) / kChC;
-  const int64_t units = (int64_t)n_seqs * n_v_heads * n_chunks;
   // one preparation block per K-head and chunk, unless that leaves fewer than
   // four per CU: then the K-head's V-heads are split over v_groups blocks
   // (the smallest divisor of the group size that fills the chip)
@@ -645,14 +660,11 @@ extern "C" int gdn_recurrence_seq_chunked(float* state, const float* q, const fl
     ++v_groups;
   const int64_t prep_blocks = k_units * v_groups;
   const int64_t scan_blocks = (int64_t)n_seqs * n_v_heads * (kChS / kChR);
-  if (units >= (int64_t(1) << 31) || scan_blocks >= (int64_t(1) << 31)) return GDN_ESIZE;
   hipStream_t s = as_stream(stream);
   float* ws = reinterpret_cast<float*>(workspace);
-  hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)prep_blocks), dim3(256), 0, s, q, k, g, beta, ws,
-                     n_tokens, n_k_heads, n_v_heads, n_chunks, v_groups);
-  int rc = launch_status();
+  const int rc = launch(chunk_prep_kernel, dim3((unsigned)prep_blocks), dim3(256), 0, s, q, k, g,
+                        beta, ws, n_tokens, n_k_heads, n_v_heads, n_chunks, v_groups);
   if (rc != GDN_OK) return rc;
-  hipLaunchKernelGGL(chunk_scan_kernel, dim3((unsigned)scan_blocks), dim3(256), 0, s, state, q, k,
-                     v, ws, y, n_tokens, n_k_heads, n_v_heads, n_chunks, scale);
-  return launch_status();
+  return launch(chunk_scan_kernel, dim3((unsigned)scan_blocks), dim3(256), 0, s, state, q, k, v,
+                ws, y, n_tokens, n_k_heads, n_v_heads, n_chunks, scale);
 }

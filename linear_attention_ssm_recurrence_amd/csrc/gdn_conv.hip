@@ -132,9 +132,8 @@ static int launch_conv_step(const float* x, const float* w, float* cs, float* ou
                             int conv_dim, hipStream_t s) {
   const int64_t total = (int64_t)n_seqs * conv_dim;
   if (grid_for(total, 256) == 0 || total / 256 >= (int64_t(1) << 31)) return GDN_ESIZE;
-  hipLaunchKernelGGL((conv_step_kernel<K>), dim3(grid_for(total, 256)), dim3(256), 0, s, x, w, cs,
-                     out, total, conv_dim);
-  return launch_status();
+  return launch(conv_step_kernel<K>, dim3(grid_for(total, 256)), dim3(256), 0, s, x, w, cs, out,
+                total, conv_dim);
 }
 
 template <int K>
@@ -146,12 +145,10 @@ static int launch_conv_scan(const float* x, const float* w, float* cs, float* ou
   const int64_t blocks = (int64_t)n_seqs * c_blocks * t_chunks;
   if (blocks >= (int64_t(1) << 31)) return GDN_ESIZE;
   if (snaps)
-    hipLaunchKernelGGL((conv_scan_kernel<K, TB, true>), dim3((unsigned)blocks), dim3(256), 0, s, x,
-                       w, cs, out, snaps, n_tokens, conv_dim, c_blocks, t_chunks);
-  else
-    hipLaunchKernelGGL((conv_scan_kernel<K, TB, false>), dim3((unsigned)blocks), dim3(256), 0, s,
-                       x, w, cs, out, nullptr, n_tokens, conv_dim, c_blocks, t_chunks);
-  return launch_status();
+    return launch(conv_scan_kernel<K, TB, true>, dim3((unsigned)blocks), dim3(256), 0, s, x, w,
+                  cs, out, snaps, n_tokens, conv_dim, c_blocks, t_chunks);
+  return launch(conv_scan_kernel<K, TB, false>, dim3((unsigned)blocks), dim3(256), 0, s, x, w, cs,
+                out, nullptr, n_tokens, conv_dim, c_blocks, t_chunks);
 }
 
 }  // namespace gdn

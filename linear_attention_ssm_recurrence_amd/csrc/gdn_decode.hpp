@@ -101,9 +101,8 @@ static int launch_decode(float* state, const float* q, const float* k, const flo
   const int64_t n_pairs = (int64_t)n_seqs * n_v_heads;
   const int64_t waves = n_pairs * (S / RW);
   const unsigned blocks = grid_for(waves, kDecodeWaves);
-  hipLaunchKernelGGL((recurrence_decode_kernel<S, RW, T4>), dim3(blocks), dim3(64 * kDecodeWaves),
-                     0, stream, state, q, k, v, g, beta, y, n_pairs, n_k_heads, n_v_heads, scale);
-  return launch_status();
+  return launch(recurrence_decode_kernel<S, RW, T4>, dim3(blocks), dim3(64 * kDecodeWaves),
+                0, stream, state, q, k, v, g, beta, y, n_pairs, n_k_heads, n_v_heads, scale);
 }
 
 }  // namespace gdn

@@ -45,7 +45,7 @@ template <int S, int RW>
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
     float* __restrict__ state, const float* __restrict__ q, const float* __restrict__ k,
     const float* __restrict__ v, const float* __restrict__ a, const float* __restrict__ b,
-    const float* __restrict__ A_log, const float* __restrict__ dt_bias, float* __restrict__ y,
+    const float* __restrict__ ssm_a, const float* __restrict__ dt_bias, float* __restrict__ y,
     int64_t n_pairs, int n_k_heads, int n_v_heads, float scale, float l2_eps) {
   using Lay = RecurLayout<S>;
   constexpr int E = Lay::E, L = Lay::L, G = Lay::G;
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
   float kk[E], qq[E];
   load_row_part<E, L>(k + kq * S, p, kk);
   load_row_part<E, L>(q + kq * S, p, qq);
-  const float av = a[pair], bv = b[pair], dtb = dt_bias[h], alog = A_log[h];
+  const float av = a[pair], bv = b[pair], dtb = dt_bias[h], sa = ssm_a[h];
   float* sp = state + pair * (int64_t)S * S;
   float4 raw[IT][E / 4];
 #pragma unroll
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
 
   l2_normalise_row<E, L>(kk, l2_eps);
   l2_normalise_row<E, L>(qq, l2_eps);
-  const float d = expf(decay_gate(av, dtb, alog));
+  const float d = expf(decay_gate(av, dtb, sa));
   const float bt = sigmoid(bv);
 
 #pragma unroll
@@ -99,16 +99,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
 
 template <int S>
 static int launch_decode_step(float* state, const float* q, const float* k, const float* v,
-                              const float* a, const float* b, const float* A_log,
+                              const float* a, const float* b, const float* ssm_a,
                               const float* dt_bias, float* y, int n_seqs, int n_k_heads,
                               int n_v_heads, float scale, float l2_eps, hipStream_t stream) {
   constexpr int RW = DecodeCfg<S>::RW;
   const int64_t n_pairs = (int64_t)n_seqs * n_v_heads;
   const int64_t waves = n_pairs * (S / RW);
-  hipLaunchKernelGGL((decode_step_kernel<S, RW>), dim3(grid_for(waves, kDecodeWaves)),
-                     dim3(64 * kDecodeWaves), 0, stream, state, q, k, v, a, b, A_log, dt_bias, y,
-                     n_pairs, n_k_heads, n_v_heads, scale, l2_eps);
-  return launch_status();
+  return launch(decode_step_kernel<S, RW>, dim3(grid_for(waves, kDecodeWaves)),
+                dim3(64 * kDecodeWaves), 0, stream, state, q, k, v, a, b, ssm_a, dt_bias, y,
+                n_pairs, n_k_heads, n_v_heads, scale, l2_eps);
 }
 
 }  // namespace gdn
@@ -116,7 +115,7 @@ static int launch_decode_step(float* state, const float* q, const float* k, cons
 using namespace gdn;
 
 extern "C" int gdn_decode_step(float* state, const float* q, const float* k, const float* v,
-                               const float* a, const float* b, const float* A_log,
+                               const float* a, const float* b, const float* ssm_a,
                                const float* dt_bias, float* y, int n_seqs, int n_k_heads,
                                int n_v_heads, int state_size, float scale, float l2_eps,
                                void* stream) {
@@ -124,7 +123,7 @@ extern "C" int gdn_decode_step(float* state, const float* q, const float* k, con
   if (n_v_heads % n_k_heads != 0) return GDN_ESIZE;
   if (!is_state_size(state_size)) return GDN_EUNSUPPORTED;
   if (n_seqs == 0) return GDN_OK;
-  if (!state || !q || !k || !v || !a || !b || !A_log || !dt_bias || !y) return GDN_ENULL;
+  if (!state || !q || !k || !v || !a || !b || !ssm_a || !dt_bias || !y) return GDN_ENULL;
   int64_t pairs, st;
   if (!mul_ok(n_seqs, n_v_heads, &pairs) || !mul_ok(pairs, (int64_t)state_size * state_size, &st))
     return GDN_ESIZE;
@@ -132,10 +131,10 @@ extern "C" int gdn_decode_step(float* state, const float* q, const float* k, con
   if (!aligned16(state) || !aligned16(q) || !aligned16(k)) return GDN_EALIGN;
   hipStream_t s = as_stream(stream);
   switch (state_size) {
-    case 32: return launch_decode_step<32>(state, q, k, v, a, b, A_log, dt_bias, y, n_seqs, n_k_heads, n_v_heads, scale, l2_eps, s);
-    case 64: return launch_decode_step<64>(state, q, k, v, a, b, A_log, dt_bias, y, n_seqs, n_k_heads, n_v_heads, scale, l2_eps, s);
-    case 128: return launch_decode_step<128>(state, q, k, v, a, b, A_log, dt_bias, y, n_seqs, n_k_heads, n_v_heads, scale, l2_eps, s);
-    case 256: return launch_decode_step<256>(state, q, k, v, a, b, A_log, dt_bias, y, n_seqs, n_k_heads, n_v_heads, scale, l2_eps, s);
+    case 32: return launch_decode_step<32>(state, q, k, v, a, b, ssm_a, dt_bias, y, n_seqs, n_k_heads, n_v_heads, scale, l2_eps, s);
+    case 64: return launch_decode_step<64>(state, q, k, v, a, b, ssm_a, dt_bias, y, n_seqs, n_k_heads, n_v_heads, scale, l2_eps, s);
+    case 128: return launch_decode_step<128>(state, q, k, v, a, b, ssm_a, dt_bias, y, n_seqs, n_k_heads, n_v_heads, scale, l2_eps, s);
+    case 256: return launch_decode_step<256>(state, q, k, v, a, b, ssm_a, dt_bias, y, n_seqs, n_k_heads, n_v_heads, scale, l2_eps, s);
   }
   return GDN_EUNSUPPORTED;
 }

@@ -88,11 +88,14 @@ __device__ __forceinline__ float softplus_guarded(float u) {
   return u > 20.0f ? u : log1pf(expf(u));
 }
 
-// g = -exp(A_log) * softplus(a + dt_bias).
-__device__ __forceinline__ float decay_gate(float a, float dt_bias, float A_log) {
-  const float ssm_a = -expf(A_log);
+// g = ssm_a * softplus(a + dt_bias), with ssm_a = -exp(A_log) <= 0 prepared
+// once per head by the caller (gdn_ssm_a), as both Foundry pages pre-bake it.
+__device__ __forceinline__ float decay_gate(float a, float dt_bias, float ssm_a) {
   return ssm_a * softplus_guarded(a + dt_bias);
 }
+
+// ssm_a = -exp(A_log): the per-head factor of the decay gate.
+__device__ __forceinline__ float ssm_a_of(float A_log) { return -expf(A_log); }
 
 // bf16 bit pattern -> float (exact).
 __device__ __forceinline__ float bf16_to_float(uint16_t h) {

@@ -7,6 +7,8 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <tuple>
+#include <utility>
 
 #include "gdn.h"
 
@@ -35,8 +37,27 @@ inline bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   return true;
 }
 
-inline int launch_status() {
-  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ELAUNCH;
+// Enqueues kernel<<<grid, block, shmem, s>>>(args...) and returns the status
+// of this launch alone: hipLaunchKernel's own return value. (hipGetLastError
+// would also report, and clear, an error left pending on the calling thread
+// by an earlier, unrelated call, and so could call a launch that was enqueued
+// a failure.) Each argument is converted to the kernel's parameter type.
+template <typename... P, size_t... I>
+inline int launch_with(void (*kernel)(P...), dim3 grid, dim3 block, size_t shmem, hipStream_t s,
+                       std::tuple<P...>& vals, std::index_sequence<I...>) {
+  void* ptrs[sizeof...(P) > 0 ? sizeof...(P) : 1] = {static_cast<void*>(&std::get<I>(vals))...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, shmem, s) ==
+                 hipSuccess
+             ? GDN_OK
+             : GDN_ELAUNCH;
+}
+
+template <typename... P, typename... A>
+inline int launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t shmem, hipStream_t s,
+                  A... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "a kernel argument is missing or extra");
+  std::tuple<P...> vals(static_cast<P>(args)...);
+  return launch_with(kernel, grid, block, shmem, s, vals, std::index_sequence_for<P...>{});
 }
 
 inline unsigned grid_for(int64_t items, int per_block) {
@@ -69,6 +90,11 @@ __device__ __forceinline__ unsigned xcd_group(unsigned bid, unsigned nblocks) {
   if (nblocks % kXcds != 0) return bid;
   return (bid % kXcds) * (nblocks / kXcds) + bid / kXcds;
 }
+
+// Size checks of the scan kernels, for shapes the caller has already found
+// valid: GDN_OK, or GDN_ESIZE when an array or a grid would be too large.
+int recurrence_size_check(int64_t n_seqs, int64_t n_tokens, int n_v_heads, int state_size);
+int chunked_size_check(int64_t n_seqs, int64_t n_tokens, int n_v_heads);
 
 // Internal launchers shared between translation units (no argument checks:
 // the calling entry point has validated everything).

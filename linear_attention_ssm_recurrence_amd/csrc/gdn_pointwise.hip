@@ -2,7 +2,10 @@
 // sigmoid of beta, the q/k L2 normalisation with the grouped-query repeat, and
 // the gated RMSNorm.
 //
-//   decay gate  g = -exp(A_log) * softplus(a + dt_bias), softplus guarded at 20
+//   ssm_a       ssm_a = -exp(A_log), the per-head factor of the gate, which
+//               both Foundry pages prepare once on the host
+//               (ssm_gated_delta.cu fc_ssm_decay_gate comment)
+//   decay gate  g = ssm_a * softplus(a + dt_bias), softplus guarded at 20
 //               (ssm_gated_delta.cu fc_ssm_decay_gate / _nx; fm_kernel_ssm.m
 //               "Decay gate")
 //   sigmoid     beta = 1 / (1 + exp(-b))          (ssm_gated_delta.cu fc_sigmoid)
@@ -22,13 +25,20 @@ namespace gdn {
 
 __global__ __launch_bounds__(256) void decay_gate_kernel(const float* __restrict__ a,
                                                          const float* __restrict__ dt_bias,
-                                                         const float* __restrict__ A_log,
+                                                         const float* __restrict__ ssm_a,
                                                          float* __restrict__ g, int n_heads,
                                                          int64_t total) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
   const int h = (int)(idx % n_heads);
-  g[idx] = decay_gate(a[idx], dt_bias[h], A_log[h]);
+  g[idx] = decay_gate(a[idx], dt_bias[h], ssm_a[h]);
+}
+
+__global__ __launch_bounds__(256) void ssm_a_kernel(const float* __restrict__ A_log,
+                                                    float* __restrict__ out, int n) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  out[idx] = ssm_a_of(A_log[idx]);
 }
 
 __global__ __launch_bounds__(256) void sigmoid_kernel(const float* x, float* y, int64_t n) {
@@ -150,38 +160,41 @@ int launch_gated_rmsnorm(const float* y, const float* w, const ZT* z, float* out
                          int head_dim, float eps, hipStream_t s) {
   if (head_dim == 128) {
     const int64_t rows_per_block = 4 * 2 * kNormIters;
-    hipLaunchKernelGGL(gated_rmsnorm_d128_kernel<ZT>, dim3(grid_for(n_rows, rows_per_block)),
-                       dim3(256), 0, s, y, w, z, out, n_rows, eps);
-  } else {
-    hipLaunchKernelGGL(gated_rmsnorm_kernel<ZT>, dim3(grid_for(n_rows, 4)), dim3(256), 0, s, y, w,
-                       z, out, n_rows, head_dim, eps);
+    return launch(gated_rmsnorm_d128_kernel<ZT>, dim3(grid_for(n_rows, rows_per_block)),
+                  dim3(256), 0, s, y, w, z, out, n_rows, eps);
   }
-  return launch_status();
+  return launch(gated_rmsnorm_kernel<ZT>, dim3(grid_for(n_rows, 4)), dim3(256), 0, s, y, w, z, out,
+                n_rows, head_dim, eps);
 }
 
 }  // namespace gdn
 
 using namespace gdn;
 
-extern "C" int gdn_decay_gate(const float* a, const float* dt_bias, const float* A_log, float* g,
+extern "C" int gdn_ssm_a(const float* A_log, float* ssm_a, int n_heads, void* stream) {
+  if (n_heads < 0) return GDN_ESIZE;
+  if (n_heads == 0) return GDN_OK;
+  if (!A_log || !ssm_a) return GDN_ENULL;
+  return launch(ssm_a_kernel, dim3(grid_for(n_heads, 256)), dim3(256), 0, as_stream(stream),
+                A_log, ssm_a, n_heads);
+}
+
+extern "C" int gdn_decay_gate(const float* a, const float* dt_bias, const float* ssm_a, float* g,
                               int n_heads, int64_t rows, void* stream) {
   int64_t total;
   if (n_heads <= 0 || rows < 0 || !mul_ok(rows, n_heads, &total)) return GDN_ESIZE;
   if (rows == 0) return GDN_OK;
-  if (!a || !dt_bias || !A_log || !g) return GDN_ENULL;
+  if (!a || !dt_bias || !ssm_a || !g) return GDN_ENULL;
   if (total / 256 >= (int64_t(1) << 31)) return GDN_ESIZE;
-  hipLaunchKernelGGL(decay_gate_kernel, dim3(grid_for(total, 256)), dim3(256), 0,
-                     as_stream(stream), a, dt_bias, A_log, g, n_heads, total);
-  return launch_status();
+  return launch(decay_gate_kernel, dim3(grid_for(total, 256)), dim3(256), 0, as_stream(stream), a,
+                dt_bias, ssm_a, g, n_heads, total);
 }
 
 extern "C" int gdn_sigmoid(const float* x, float* y, int64_t n, void* stream) {
   if (n < 0 || n > kMaxElems || n / 256 >= (int64_t(1) << 31)) return GDN_ESIZE;
   if (n == 0) return GDN_OK;
   if (!x || !y) return GDN_ENULL;
-  hipLaunchKernelGGL(sigmoid_kernel, dim3(grid_for(n, 256)), dim3(256), 0, as_stream(stream), x,
-                     y, n);
-  return launch_status();
+  return launch(sigmoid_kernel, dim3(grid_for(n, 256)), dim3(256), 0, as_stream(stream), x, y, n);
 }
 
 extern "C" int gdn_l2norm_gqa(const float* x, float* out, int64_t rows, int n_k_heads,
@@ -196,9 +209,8 @@ extern "C" int gdn_l2norm_gqa(const float* x, float* out, int64_t rows, int n_k_
     return GDN_ESIZE;
   if (groups / 4 >= (int64_t(1) << 31)) return GDN_ESIZE;
   if (!aligned16(x) || !aligned16(out)) return GDN_EALIGN;
-  hipLaunchKernelGGL(l2norm_gqa_kernel, dim3(grid_for(groups, 4)), dim3(256), 0,
-                     as_stream(stream), x, out, groups, n_k_heads, n_v_heads, head_dim, eps);
-  return launch_status();
+  return launch(l2norm_gqa_kernel, dim3(grid_for(groups, 4)), dim3(256), 0, as_stream(stream), x,
+                out, groups, n_k_heads, n_v_heads, head_dim, eps);
 }
 
 extern "C" int gdn_gated_rmsnorm(const float* y, const float* w, const float* z, float* out,

@@ -78,7 +78,7 @@ __device__ __forceinline__ void load_bf16x4(const uint16_t* p, float (&x)[4]) {
 template <int K>
 __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_frontend_kernel(
     const uint16_t* __restrict__ qkv, const float* __restrict__ a, const float* __restrict__ b,
-    const float* __restrict__ conv_w, const float* __restrict__ A_log,
+    const float* __restrict__ conv_w, const float* __restrict__ ssm_a,
     const float* __restrict__ dt_bias, float* __restrict__ conv_state, float* __restrict__ qo,
     float* __restrict__ ko, float* __restrict__ vo, float* __restrict__ go,
     float* __restrict__ bo, int n_tokens, int n_k_heads, int n_v_heads, int t_chunks,
@@ -161,12 +161,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_frontend_kernel(
   // the decay gate and beta inputs of the wave's positions (v parts)
   const bool gate_lane = (kind == 2 && lane < TB && t0 + lane < n_tokens);
   const int64_t gidx = (n * (int64_t)n_tokens + (gate_lane ? t0 + lane : 0)) * n_v_heads + head;
-  float ga = 0.0f, gb = 0.0f, gdt = 0.0f, gal = 0.0f;
+  float ga = 0.0f, gb = 0.0f, gdt = 0.0f, gsa = 0.0f;
   if (gate_lane) {
     ga = a[gidx];
     gb = b[gidx];
     gdt = dt_bias[head];
-    gal = A_log[head];
+    gsa = ssm_a[head];
   }
 
   const int64_t HKS = (int64_t)n_k_heads * S, HS = (int64_t)n_v_heads * S;
@@ -215,24 +215,28 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_frontend_kernel(
   }
   // decay gate and beta of the wave's positions, by the v parts
   if (gate_lane) {
-    go[gidx] = decay_gate(ga, gdt, gal);
+    go[gidx] = decay_gate(ga, gdt, gsa);
     bo[gidx] = sigmoid(gb);
   }
 }
 
+inline int64_t frontend_blocks(int64_t n_seqs, int64_t n_tokens, int64_t n_k_heads,
+                               int64_t n_v_heads) {
+  return n_seqs * ((n_tokens + kPrefillTB - 1) / kPrefillTB) *
+         ((2 * n_k_heads + n_v_heads + kPrefillWaves - 1) / kPrefillWaves);
+}
+
 template <int K>
 static int launch_frontend(const uint16_t* qkv, const float* a, const float* b,
-                           const float* conv_w, const float* A_log, const float* dt_bias,
+                           const float* conv_w, const float* ssm_a, const float* dt_bias,
                            float* conv_state, const PrefillWorkspace& ws, int n_seqs, int n_tokens,
                            int n_k_heads, int n_v_heads, float l2_eps, hipStream_t s) {
   const int t_chunks = (n_tokens + kPrefillTB - 1) / kPrefillTB;
   const int part_blocks = (2 * n_k_heads + n_v_heads + kPrefillWaves - 1) / kPrefillWaves;
-  const int64_t blocks = (int64_t)n_seqs * t_chunks * part_blocks;
-  if (blocks >= (int64_t(1) << 31)) return GDN_ESIZE;
-  hipLaunchKernelGGL((prefill_frontend_kernel<K>), dim3((unsigned)blocks), dim3(64 * kPrefillWaves),
-                     0, s, qkv, a, b, conv_w, A_log, dt_bias, conv_state, ws.q, ws.k, ws.v, ws.g,
-                     ws.beta, n_tokens, n_k_heads, n_v_heads, t_chunks, part_blocks, l2_eps);
-  return launch_status();
+  const int64_t blocks = frontend_blocks(n_seqs, n_tokens, n_k_heads, n_v_heads);
+  return launch(prefill_frontend_kernel<K>, dim3((unsigned)blocks), dim3(64 * kPrefillWaves),
+                0, s, qkv, a, b, conv_w, ssm_a, dt_bias, conv_state, ws.q, ws.k, ws.v, ws.g,
+                ws.beta, n_tokens, n_k_heads, n_v_heads, t_chunks, part_blocks, l2_eps);
 }
 
 }  // namespace gdn
@@ -246,7 +250,7 @@ extern "C" size_t gdn_prefill_workspace_bytes(int n_seqs, int n_tokens, int n_k_
 }
 
 extern "C" int gdn_prefill_bf16_ex(const uint16_t* qkv, const uint16_t* z, const float* a,
-                                   const float* b, const float* conv_w, const float* A_log,
+                                   const float* b, const float* conv_w, const float* ssm_a,
                                    const float* dt_bias, const float* norm_w, float* conv_state,
                                    float* state, float* out, void* workspace,
                                    size_t workspace_bytes, int n_seqs, int n_tokens,
@@ -259,7 +263,7 @@ extern "C" int gdn_prefill_bf16_ex(const uint16_t* qkv, const uint16_t* z, const
   if (n_v_heads % n_k_heads != 0) return GDN_ESIZE;
   if (state_size != kPrefillS || conv_kernel < 2 || conv_kernel > 4) return GDN_EUNSUPPORTED;
   if (n_seqs == 0 || n_tokens == 0) return GDN_OK;
-  if (!qkv || !z || !a || !b || !conv_w || !A_log || !dt_bias || !norm_w || !conv_state ||
+  if (!qkv || !z || !a || !b || !conv_w || !ssm_a || !dt_bias || !norm_w || !conv_state ||
       !state || !out || !workspace)
     return GDN_ENULL;
   int64_t rows, elems;
@@ -272,15 +276,22 @@ extern "C" int gdn_prefill_bf16_ex(const uint16_t* qkv, const uint16_t* z, const
   if (!aligned16(state) || !aligned16(norm_w) || !aligned16(out)) return GDN_EALIGN;
   if ((reinterpret_cast<uintptr_t>(z) & 7u) != 0 || (reinterpret_cast<uintptr_t>(qkv) & 7u) != 0)
     return GDN_EALIGN;
+  // the scan's and the norm's own limits, checked here so that a call they
+  // would refuse launches nothing (the front end rolls conv_state in place)
+  if (recurrence_size_check(n_seqs, n_tokens, n_v_heads, state_size) != GDN_OK) return GDN_ESIZE;
+  if (scan == GDN_SCAN_CHUNKED && chunked_size_check(n_seqs, n_tokens, n_v_heads) != GDN_OK)
+    return GDN_ESIZE;
+  if (frontend_blocks(n_seqs, n_tokens, n_k_heads, n_v_heads) >= (int64_t(1) << 31))
+    return GDN_ESIZE;
   PrefillWorkspace ws;
   prefill_layout(n_seqs, n_tokens, n_k_heads, n_v_heads, state_size,
                  reinterpret_cast<char*>(workspace), &ws);
   hipStream_t s = as_stream(stream);
   int rc = GDN_EUNSUPPORTED;
   switch (conv_kernel) {
-    case 2: rc = launch_frontend<2>(qkv, a, b, conv_w, A_log, dt_bias, conv_state, ws, n_seqs, n_tokens, n_k_heads, n_v_heads, l2_eps, s); break;
-    case 3: rc = launch_frontend<3>(qkv, a, b, conv_w, A_log, dt_bias, conv_state, ws, n_seqs, n_tokens, n_k_heads, n_v_heads, l2_eps, s); break;
-    case 4: rc = launch_frontend<4>(qkv, a, b, conv_w, A_log, dt_bias, conv_state, ws, n_seqs, n_tokens, n_k_heads, n_v_heads, l2_eps, s); break;
+    case 2: rc = launch_frontend<2>(qkv, a, b, conv_w, ssm_a, dt_bias, conv_state, ws, n_seqs, n_tokens, n_k_heads, n_v_heads, l2_eps, s); break;
+    case 3: rc = launch_frontend<3>(qkv, a, b, conv_w, ssm_a, dt_bias, conv_state, ws, n_seqs, n_tokens, n_k_heads, n_v_heads, l2_eps, s); break;
+    case 4: rc = launch_frontend<4>(qkv, a, b, conv_w, ssm_a, dt_bias, conv_state, ws, n_seqs, n_tokens, n_k_heads, n_v_heads, l2_eps, s); break;
   }
   if (rc != GDN_OK) return rc;
   if (scan == GDN_SCAN_CHUNKED)
@@ -296,13 +307,13 @@ extern "C" int gdn_prefill_bf16_ex(const uint16_t* qkv, const uint16_t* z, const
 }
 
 extern "C" int gdn_prefill_bf16(const uint16_t* qkv, const uint16_t* z, const float* a,
-                                const float* b, const float* conv_w, const float* A_log,
+                                const float* b, const float* conv_w, const float* ssm_a,
                                 const float* dt_bias, const float* norm_w, float* conv_state,
                                 float* state, float* out, void* workspace, size_t workspace_bytes,
                                 int n_seqs, int n_tokens, int n_k_heads, int n_v_heads,
                                 int state_size, int conv_kernel, float scale, float l2_eps,
                                 float eps, void* stream) {
-  return gdn_prefill_bf16_ex(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out,
+  return gdn_prefill_bf16_ex(qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state, state, out,
                              workspace, workspace_bytes, n_seqs, n_tokens, n_k_heads, n_v_heads,
                              state_size, conv_kernel, scale, l2_eps, eps, GDN_SCAN_SEQUENTIAL,
                              stream);

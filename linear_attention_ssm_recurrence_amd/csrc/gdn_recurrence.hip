@@ -135,10 +135,9 @@ static int launch_short_scan(float* state, const float* q, const float* k, const
   constexpr int RW = DecodeCfg<S>::RW;
   const int64_t n_pairs = (int64_t)n_seqs * n_v_heads;
   const unsigned blocks = grid_for(n_pairs * (S / RW), kDecodeWaves);
-  hipLaunchKernelGGL((recurrence_short_scan_kernel<S, RW, SNAP, T4>), dim3(blocks),
-                     dim3(64 * kDecodeWaves), 0, stream, state, q, k, v, g, beta, y, snaps, n_pairs,
-                     n_tokens, n_k_heads, n_v_heads, scale);
-  return launch_status();
+  return launch(recurrence_short_scan_kernel<S, RW, SNAP, T4>, dim3(blocks),
+                dim3(64 * kDecodeWaves), 0, stream, state, q, k, v, g, beta, y, snaps, n_pairs,
+                n_tokens, n_k_heads, n_v_heads, scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -388,14 +387,23 @@ static int launch_scan(float* state, const float* q, const float* k, const float
   static_assert(CfgL::BPH == CfgS::BPH && CfgL::THREADS == CfgS::THREADS, "same grid either way");
   const int64_t blocks = (int64_t)n_seqs * n_v_heads * CfgL::BPH;
   if (blocks <= cu_count())
-    hipLaunchKernelGGL((recurrence_scan_kernel<S, true, SNAP, T4>), dim3((unsigned)blocks),
-                       dim3(CfgL::THREADS), 0, stream, state, q, k, v, g, beta, y, snaps, n_tokens,
-                       n_k_heads, n_v_heads, scale);
-  else
-    hipLaunchKernelGGL((recurrence_scan_kernel<S, false, SNAP, T4>), dim3((unsigned)blocks),
-                       dim3(CfgS::THREADS), 0, stream, state, q, k, v, g, beta, y, snaps, n_tokens,
-                       n_k_heads, n_v_heads, scale);
-  return launch_status();
+    return launch(recurrence_scan_kernel<S, true, SNAP, T4>, dim3((unsigned)blocks),
+                  dim3(CfgL::THREADS), 0, stream, state, q, k, v, g, beta, y, snaps, n_tokens,
+                  n_k_heads, n_v_heads, scale);
+  return launch(recurrence_scan_kernel<S, false, SNAP, T4>, dim3((unsigned)blocks),
+                dim3(CfgS::THREADS), 0, stream, state, q, k, v, g, beta, y, snaps, n_tokens,
+                n_k_heads, n_v_heads, scale);
+}
+
+// Array sizes and grid limits of the decode and scan kernels, for shapes that
+// are otherwise valid (also used by the prefill before it launches anything).
+int recurrence_size_check(int64_t n_seqs, int64_t n_tokens, int n_v_heads, int state_size) {
+  int64_t pairs, st, vec;
+  if (!mul_ok(n_seqs, n_v_heads, &pairs) || !mul_ok(pairs, (int64_t)state_size * state_size, &st) ||
+      !mul_ok(pairs * n_tokens, state_size, &vec))
+    return GDN_ESIZE;
+  if (pairs * (state_size / 8) / kDecodeWaves >= (int64_t(1) << 31)) return GDN_ESIZE;  // grid limit
+  return GDN_OK;
 }
 
 static int check_recurrence(float* state, const float* q, const float* k, const float* v,
@@ -407,11 +415,7 @@ static int check_recurrence(float* state, const float* q, const float* k, const 
   if (!is_state_size(state_size)) return GDN_EUNSUPPORTED;
   if (n_seqs == 0 || n_tokens == 0) return kNothingToDo;
   if (!state || !q || !k || !v || !g || !beta || !y) return GDN_ENULL;
-  int64_t pairs, st, vec;
-  if (!mul_ok(n_seqs, n_v_heads, &pairs) || !mul_ok(pairs, (int64_t)state_size * state_size, &st) ||
-      !mul_ok(pairs * n_tokens, state_size, &vec))
-    return GDN_ESIZE;
-  if (pairs * (state_size / 8) / kDecodeWaves >= (int64_t(1) << 31)) return GDN_ESIZE;  // grid limit
+  if (recurrence_size_check(n_seqs, n_tokens, n_v_heads, state_size) != GDN_OK) return GDN_ESIZE;
   if (!aligned16(state) || !aligned16(q) || !aligned16(k)) return GDN_EALIGN;
   return GDN_OK;
 }

@@ -68,7 +68,7 @@ def load_library():
         "gdn_prefill_bf16": [P] * 12 + [ctypes.c_size_t] + [I] * 6 + [F] * 3 + [P],
         "gdn_prefill_bf16_ex": [P] * 12 + [ctypes.c_size_t] + [I] * 6 + [F] * 3 + [I, P],
         "gdn_recurrence_seq_chunked": [P] * 8 + [ctypes.c_size_t] + [I] * 5 + [F, P],
-        "gdn_probe_fma": [P, I, I, F, F, P],
+        "gdn_ssm_a": [P, P, I, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -160,13 +160,24 @@ F32 = torch.float32
 
 
 @_typed
-def gdn_decay_gate(a, dt_bias, A_log, g, stream=None):
-    """g[..., h] = -exp(A_log[h]) * softplus(a[..., h] + dt_bias[h])."""
-    H = A_log.shape[0]
+def gdn_ssm_a(A_log, ssm_a, stream=None):
+    """ssm_a[h] = -exp(A_log[h]), the gate's per-head factor (prepared once
+    per layer's parameters); A_log, ssm_a [H]."""
+    H = A_log.numel()
+    _shape(A_log, (H,), "A_log")
+    _shape(ssm_a, (H,), "ssm_a")
+    _call("gdn_ssm_a", _ptr(A_log, F32, "A_log"), _ptr(ssm_a, F32, "ssm_a"), H,
+          _stream(A_log, stream))
+
+
+@_typed
+def gdn_decay_gate(a, dt_bias, ssm_a, g, stream=None):
+    """g[..., h] = ssm_a[h] * softplus(a[..., h] + dt_bias[h]), ssm_a = -exp(A_log)."""
+    H = ssm_a.shape[0]
     _shape(dt_bias, (H,), "dt_bias")
     _shape(g, a.shape, "g")
     _call("gdn_decay_gate", _ptr(a, F32, "a"), _ptr(dt_bias, F32, "dt_bias"),
-          _ptr(A_log, F32, "A_log"), _ptr(g, F32, "g"), H, a.numel() // max(H, 1),
+          _ptr(ssm_a, F32, "ssm_a"), _ptr(g, F32, "g"), H, a.numel() // max(H, 1),
           _stream(a, stream))
 
 
@@ -258,10 +269,10 @@ def gdn_recurrence_ex(state, q, k, v, g, beta, y, scale, variant=GDN_RECUR_EXACT
 
 
 @_typed
-def gdn_decode_step(state, q, k, v, a, b, A_log, dt_bias, y, scale, l2_eps=1e-6, stream=None):
+def gdn_decode_step(state, q, k, v, a, b, ssm_a, dt_bias, y, scale, l2_eps=1e-6, stream=None):
     """One decode step from raw inputs: state [N][H][S][S] in place; q, k
     [N][HK][S] raw (normalised in the kernel); v, y [N][H][S]; a, b [N][H];
-    A_log, dt_bias [H]."""
+    ssm_a, dt_bias [H]."""
     N, H, S = v.shape
     HK = q.shape[1]
     _shape(state, (N, H, S, S), "state")
@@ -270,10 +281,10 @@ def gdn_decode_step(state, q, k, v, a, b, A_log, dt_bias, y, scale, l2_eps=1e-6,
     _shape(y, (N, H, S), "y")
     _shape(a, (N, H), "a")
     _shape(b, (N, H), "b")
-    _shape(A_log, (H,), "A_log")
+    _shape(ssm_a, (H,), "ssm_a")
     _shape(dt_bias, (H,), "dt_bias")
     _call("gdn_decode_step", _ptr(state, F32, "state"), _ptr(q, F32, "q"), _ptr(k, F32, "k"),
-          _ptr(v, F32, "v"), _ptr(a, F32, "a"), _ptr(b, F32, "b"), _ptr(A_log, F32, "A_log"),
+          _ptr(v, F32, "v"), _ptr(a, F32, "a"), _ptr(b, F32, "b"), _ptr(ssm_a, F32, "ssm_a"),
           _ptr(dt_bias, F32, "dt_bias"), _ptr(y, F32, "y"), N, HK, H, S, float(scale),
           float(l2_eps), _stream(v, stream))
 
@@ -332,18 +343,18 @@ def gdn_gated_rmsnorm(y, w, z, out, eps=1e-6, stream=None):
 
 
 @_typed
-def gdn_decode_block_bf16(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out,
+def gdn_decode_block_bf16(qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state, state, out,
                           n_k_heads, scale, l2_eps=1e-6, eps=1e-6, stream=None):
     """One fused decode layer. qkv [N][C] and z [N][H][S] hold bf16 bit patterns
     (int16/uint16 tensors, or torch.bfloat16); the rest are fp32:
-    a, b [N][H]; conv_w [C][K]; A_log, dt_bias [H]; norm_w [S];
+    a, b [N][H]; conv_w [C][K]; ssm_a, dt_bias [H]; norm_w [S];
     conv_state [N][C][K-1] and state [N][H][S][S] updated in place; out [N][H][S]."""
     N, H, S = z.shape
     C, K = conv_w.shape
-    _block_shapes(qkv, a, b, A_log, dt_bias, norm_w, conv_state, state, out, N, H, S, C, K,
+    _block_shapes(qkv, a, b, ssm_a, dt_bias, norm_w, conv_state, state, out, N, H, S, C, K,
                   n_k_heads)
     _call("gdn_decode_block_bf16", _ptr16(qkv, "qkv"), _ptr16(z, "z"), _ptr(a, F32, "a"),
-          _ptr(b, F32, "b"), _ptr(conv_w, F32, "conv_w"), _ptr(A_log, F32, "A_log"),
+          _ptr(b, F32, "b"), _ptr(conv_w, F32, "conv_w"), _ptr(ssm_a, F32, "ssm_a"),
           _ptr(dt_bias, F32, "dt_bias"), _ptr(norm_w, F32, "norm_w"),
           _ptr(conv_state, F32, "conv_state"), _ptr(state, F32, "state"), _ptr(out, F32, "out"),
           N, n_k_heads, H, S, K, float(scale), float(l2_eps), float(eps), _stream(z, stream))
@@ -354,7 +365,7 @@ def gdn_decode_block_workspace_bytes(n_seqs, n_k_heads, n_v_heads) -> int:
 
 
 @_typed
-def gdn_decode_block_bf16_ex(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state,
+def gdn_decode_block_bf16_ex(qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state, state,
                              out, workspace, n_k_heads, scale, l2_eps=1e-6, eps=1e-6,
                              stream=None):
     """gdn_decode_block_bf16 with the state split over 64-row workgroups.
@@ -363,22 +374,22 @@ def gdn_decode_block_bf16_ex(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_
     is zero before the first call (every completed call leaves it zero)."""
     N, H, S = z.shape
     C, K = conv_w.shape
-    _block_shapes(qkv, a, b, A_log, dt_bias, norm_w, conv_state, state, out, N, H, S, C, K,
+    _block_shapes(qkv, a, b, ssm_a, dt_bias, norm_w, conv_state, state, out, N, H, S, C, K,
                   n_k_heads)
     _call("gdn_decode_block_bf16_ex", _ptr16(qkv, "qkv"), _ptr16(z, "z"), _ptr(a, F32, "a"),
-          _ptr(b, F32, "b"), _ptr(conv_w, F32, "conv_w"), _ptr(A_log, F32, "A_log"),
+          _ptr(b, F32, "b"), _ptr(conv_w, F32, "conv_w"), _ptr(ssm_a, F32, "ssm_a"),
           _ptr(dt_bias, F32, "dt_bias"), _ptr(norm_w, F32, "norm_w"),
           _ptr(conv_state, F32, "conv_state"), _ptr(state, F32, "state"), _ptr(out, F32, "out"),
           _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
           N, n_k_heads, H, S, K, float(scale), float(l2_eps), float(eps), _stream(z, stream))
 
 
-def _block_shapes(qkv, a, b, A_log, dt_bias, norm_w, conv_state, state, out, N, H, S, C, K,
+def _block_shapes(qkv, a, b, ssm_a, dt_bias, norm_w, conv_state, state, out, N, H, S, C, K,
                   n_k_heads):
     _shape(qkv, (N, C), "qkv")
     for t, nm in ((a, "a"), (b, "b")):
         _shape(t, (N, H), nm)
-    _shape(A_log, (H,), "A_log")
+    _shape(ssm_a, (H,), "ssm_a")
     _shape(dt_bias, (H,), "dt_bias")
     _shape(norm_w, (S,), "norm_w")
     _shape(conv_state, (N, C, K - 1), "conv_state")
@@ -400,10 +411,10 @@ def gdn_prefill_workspace_bytes(n_seqs, n_tokens, n_k_heads, n_v_heads, state_si
 
 
 @_typed
-def gdn_prefill_bf16(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, state, out,
+def gdn_prefill_bf16(qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state, state, out,
                      workspace, n_k_heads, scale, l2_eps=1e-6, eps=1e-6, stream=None, scan=None):
     """One layer over T positions. qkv [N][T][C] and z [N][T][H][S] hold bf16
-    bit patterns; a, b [N][T][H]; conv_w [C][K]; A_log, dt_bias [H]; norm_w [S];
+    bit patterns; a, b [N][T][H]; conv_w [C][K]; ssm_a, dt_bias [H]; norm_w [S];
     conv_state [N][C][K-1] and state [N][H][S][S] updated in place;
     out [N][T][H][S]; workspace a uint8 device tensor of at least
     gdn_prefill_workspace_bytes(...) bytes. scan=None calls gdn_prefill_bf16;
@@ -413,7 +424,7 @@ def gdn_prefill_bf16(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, s
     _shape(qkv, (N, T, C), "qkv")
     for t, nm in ((a, "a"), (b, "b")):
         _shape(t, (N, T, H), nm)
-    _shape(A_log, (H,), "A_log")
+    _shape(ssm_a, (H,), "ssm_a")
     _shape(dt_bias, (H,), "dt_bias")
     _shape(norm_w, (S,), "norm_w")
     _shape(conv_state, (N, C, K - 1), "conv_state")
@@ -422,7 +433,7 @@ def gdn_prefill_bf16(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state, s
     if C != 2 * n_k_heads * S + H * S:
         raise ValueError(f"conv_dim {C} != 2*n_k_heads*S + n_v_heads*S")
     args = (_ptr16(qkv, "qkv"), _ptr16(z, "z"), _ptr(a, F32, "a"),
-            _ptr(b, F32, "b"), _ptr(conv_w, F32, "conv_w"), _ptr(A_log, F32, "A_log"),
+            _ptr(b, F32, "b"), _ptr(conv_w, F32, "conv_w"), _ptr(ssm_a, F32, "ssm_a"),
             _ptr(dt_bias, F32, "dt_bias"), _ptr(norm_w, F32, "norm_w"),
             _ptr(conv_state, F32, "conv_state"), _ptr(state, F32, "state"), _ptr(out, F32, "out"),
             _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), N, T, n_k_heads, H, S, K,
@@ -454,15 +465,3 @@ def gdn_recurrence_seq_chunked(state, q, k, v, g, beta, y, scale, workspace, str
           _ptr(k, F32, "k"), _ptr(v, F32, "v"), _ptr(g, F32, "g"), _ptr(beta, F32, "beta"),
           _ptr(y, F32, "y"), _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
           N, T, HK, H, S, float(scale), _stream(v, stream))
-
-
-@_typed
-def gdn_probe_fma(out, iters, a=0.999, b=1e-3, stream=None):
-    """Measurement probe (not a step of the method): out is a float32 device
-    tensor of n_blocks * 256 elements; runs n_blocks * 256 * iters * 32 flop
-    of dependent fp32 FMA chains."""
-    n = out.numel()
-    if n % 256 != 0:
-        raise ValueError("out must hold n_blocks * 256 floats")
-    _call("gdn_probe_fma", _ptr(out, F32, "out"), n // 256, int(iters), float(a), float(b),
-          _stream(out, stream))

@@ -1,6 +1,6 @@
 /*
  * A plain C caller of the library, built by tests/test_abi_cpu.py as strict
- * C11 and as C++17 against include/gdn.h and include/gdn_probe.h and linked
+ * C11 and as C++17 against include/gdn.h and linked
  * with libgdn.so. Every entry point is called once or more on an argument
  * path that returns before anything is launched (no GPU is needed), through
  * the header's own prototypes, and the return code is checked. A header that
@@ -13,7 +13,6 @@
 #include <stdio.h>
 
 #include "gdn.h"
-#include "gdn_probe.h"
 
 static int failures = 0;
 
@@ -120,8 +119,10 @@ int main(void) {
                                     NULL),
          GDN_EUNSUPPORTED);
 
-  EXPECT(gdn_probe_fma(NULL, 1, 1, 1.0f, 0.0f, NULL), GDN_ENULL);
-  EXPECT(gdn_probe_fma(f, 0, 1, 1.0f, 0.0f, NULL), GDN_ESIZE);
+  EXPECT(gdn_ssm_a(NULL, f, 4, NULL), GDN_ENULL);
+  EXPECT(gdn_ssm_a(cf, NULL, 4, NULL), GDN_ENULL);
+  EXPECT(gdn_ssm_a(cf, f, -1, NULL), GDN_ESIZE);
+  EXPECT(gdn_ssm_a(NULL, NULL, 0, NULL), GDN_OK);
 
   printf("%d failures\n", failures);
   return failures != 0;

@@ -188,6 +188,7 @@ static void fused_paths(hipStream_t stream) {
   float *d_qr = dev_copy(qr, nkq), *d_kr = dev_copy(kr, nkq), *d_v = dev_copy(v, nv);
   float *d_a = dev_copy(a, (size_t)N * H), *d_b = dev_copy(b, (size_t)N * H);
   float *d_Al = dev_copy(A_log, (size_t)H), *d_dt = dev_copy(dt_bias, (size_t)H);
+  GDN_OK_CALL(gdn_ssm_a(d_Al, d_Al, H, stream)); /* in place: d_Al now holds ssm_a = -exp(A_log) */
   float *d_y1 = dev_copy(NULL, nv), *d_y2 = dev_copy(NULL, nv);
   float *d_q = dev_copy(NULL, nv), *d_k = dev_copy(NULL, nv);
   float *d_g = dev_copy(NULL, (size_t)N * H), *d_be = dev_copy(NULL, (size_t)N * H);

@@ -33,6 +33,26 @@ def dev_bits(x) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint16).view(np.int16)).to(DEV)
 
 
+def dev_ssm_a(A_log) -> torch.Tensor:
+    """The gate's per-head factor ssm_a = -exp(A_log) on the device, from the
+    library's own kernel (gdn_ssm_a): the form every gate-forming entry point
+    takes. A_log is a host array or a device tensor."""
+    from linear_attention_ssm_recurrence_amd import gdn
+    t = A_log if isinstance(A_log, torch.Tensor) else dev(A_log)
+    out = torch.empty_like(t)
+    gdn.gdn_ssm_a(t, out)
+    torch.cuda.current_stream(out.device).synchronize()   # ready for any stream
+    return out
+
+
+def upload_layer(lb: dict) -> dict:
+    """A fused-layer input dict on the device (bf16 patterns as int16), with
+    ssm_a from the library beside A_log."""
+    t = {key: (dev_bits(val) if val.dtype == np.uint16 else dev(val)) for key, val in lb.items()}
+    t["ssm_a"] = dev_ssm_a(t["A_log"])
+    return t
+
+
 def host(t: torch.Tensor) -> np.ndarray:
     torch.cuda.synchronize()
     return t.detach().cpu().numpy()

@@ -39,7 +39,7 @@ def test_exports_every_header_symbol(lib):
 @pytest.mark.parametrize("std", ["c11", "c++17"])
 def test_c_consumer(lib, tmp_path, std):
     """tests/abi_consumer.c, a plain C caller, builds as strict C11 and as
-    C++17 against include/gdn.h and include/gdn_probe.h, links against
+    C++17 against include/gdn.h, links against
     libgdn.so (every declared function must resolve), and gets the expected
     code from each entry point's argument checks through the header's own
     prototypes. None of its calls passes validation, so nothing is launched."""
@@ -257,12 +257,43 @@ def test_prefill_validation(lib):
     assert call(first=NUL, ws=NUL, T=0) == gdn.GDN_OK
 
 
-def test_probe_validation(lib):
-    f = lib.gdn_probe_fma
-    assert f(FAKE, 0, 10, 1.0, 0.0, NUL) == gdn.GDN_ESIZE
-    assert f(FAKE, 4, 0, 1.0, 0.0, NUL) == gdn.GDN_ESIZE
-    assert f(FAKE, (1 << 20) + 1, 10, 1.0, 0.0, NUL) == gdn.GDN_ESIZE
-    assert f(NUL, 4, 10, 1.0, 0.0, NUL) == gdn.GDN_ENULL
+def test_probe_is_not_in_the_library(lib):
+    """The benchmark's FMA probe lives in its own library, libgdn_probe.so,
+    not among libgdn.so's exports; its argument checks return before any
+    launch."""
+    out = os.popen(f"nm -D --defined-only {gdn.LIB_PATH}").read()
+    assert "gdn_probe_fma" not in out
+    path = os.path.join(os.path.dirname(gdn.LIB_PATH), "libgdn_probe.so")
+    probe = ctypes.CDLL(path)
+    f = probe.gdn_probe_fma
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_float,
+                  ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(FAKE, 0, 10, 1.0, 0.0, NUL) == 2
+    assert f(FAKE, 4, 0, 1.0, 0.0, NUL) == 2
+    assert f(FAKE, (1 << 20) + 1, 10, 1.0, 0.0, NUL) == 2
+    assert f(NUL, 4, 10, 1.0, 0.0, NUL) == 1
+
+
+def test_ssm_a_validation(lib):
+    f = lib.gdn_ssm_a
+    assert f(NUL, FAKE, 4, NUL) == gdn.GDN_ENULL
+    assert f(FAKE, NUL, 4, NUL) == gdn.GDN_ENULL
+    assert f(FAKE, FAKE, -1, NUL) == gdn.GDN_ESIZE
+    assert f(NUL, NUL, 0, NUL) == gdn.GDN_OK
+
+
+def test_prefill_checks_the_scan_before_launching(lib):
+    """A prefill whose chunked scan would exceed its grid limit (8 blocks per
+    (sequence, V-head): 2^22 sequences x 64 heads) is refused with GDN_ESIZE
+    before the front end (which rolls conv_state in place) is launched: a
+    launch on this host, which has no GPU, would have returned GDN_ELAUNCH."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("argument-check test for a host without a GPU")
+    N, T, HK, H = 1 << 22, 1, 64, 64
+    args = [FAKE] * 11 + [FAKE, ctypes.c_size_t(1 << 62), N, T, HK, H, 128, 4, 0.1, 1e-6, 1e-6]
+    assert lib.gdn_prefill_bf16_ex(*args, gdn.GDN_SCAN_CHUNKED, NUL) == gdn.GDN_ESIZE
 
 
 def test_prefill_ex_validation(lib):

@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import DEV, assert_close, dev, dev_bits, host, oracle_threads
+from gpu_helpers import DEV, assert_close, dev_ssm_a, dev, dev_bits, host, oracle_threads
 from linear_attention_ssm_recurrence_amd import gdn, inputs
 
 pytestmark = pytest.mark.gpu
@@ -63,7 +63,8 @@ class _Pair:
     """The same layer's buffers twice on the device: one set for each entry point."""
 
     def __init__(self, d):
-        self.fixed = {k: dev(d[k]) for k in ("conv_w", "A_log", "dt_bias", "norm_w")}
+        self.fixed = {k: dev(d[k]) for k in ("conv_w", "dt_bias", "norm_w")}
+        self.fixed["ssm_a"] = dev_ssm_a(d["A_log"])
         N, H, S = d["z"].shape
         self.one = {"conv_state": dev(d["conv_state"]), "state": dev(d["state"]),
                     "out": torch.empty((N, H, S), dtype=torch.float32, device=DEV)}
@@ -75,7 +76,7 @@ class _Pair:
         f = self.fixed
         for bufs, fn, extra in ((self.one, gdn.gdn_decode_block_bf16, ()),
                                 (self.split, gdn.gdn_decode_block_bf16_ex, (ws,))):
-            fn(qkv, z, a, b, f["conv_w"], f["A_log"], f["dt_bias"], f["norm_w"],
+            fn(qkv, z, a, b, f["conv_w"], f["ssm_a"], f["dt_bias"], f["norm_w"],
                bufs["conv_state"], bufs["state"], bufs["out"], *extra, HK, scale, 1e-6, 1e-6)
 
     def assert_equal(self, what):

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import DEV, assert_close, dev, host, oracle_threads
+from gpu_helpers import DEV, assert_close, dev_ssm_a, dev, host, oracle_threads
 from linear_attention_ssm_recurrence_amd import gdn, inputs
 
 pytestmark = pytest.mark.gpu
@@ -51,7 +51,7 @@ def _check_steps(N, HK, H, S, steps, seed, zero_qk=False, extreme_gate=False, l2
                              -80.0, 0.0]
             x["b"][0, :6] = [1e30, -1e30, 60.0, -60.0, 0.0, 1.0]
         d = {key: dev(val) for key, val in x.items()}
-        Al, db = dev(A_log), dev(dt_bias)
+        Al, db = dev_ssm_a(A_log), dev(dt_bias)
         y = torch.empty((N, H, S), device=DEV)
         gdn.gdn_decode_step(st_fused, d["q"], d["k"], d["v"], d["a"], d["b"], Al, db, y, scale,
                             l2_eps)

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import DEV, dev
+from gpu_helpers import DEV, dev, dev_ssm_a, upload_layer
 from linear_attention_ssm_recurrence_amd import gdn, inputs
 
 pytestmark = pytest.mark.gpu
@@ -39,13 +39,13 @@ def test_decode_step_graph_replays_equal_eager():
     beta = torch.empty((1, H), device=DEV)
     gdn.gdn_l2norm_gqa(dev(d["q_raw"][:, 0]), q, w.l2_eps)
     gdn.gdn_l2norm_gqa(dev(d["k_raw"][:, 0]), k, w.l2_eps)
-    gdn.gdn_decay_gate(dev(d["a"][:, 0]), dev(d["dt_bias"]), dev(d["A_log"]), g)
+    gdn.gdn_decay_gate(dev(d["a"][:, 0]), dev(d["dt_bias"]), dev_ssm_a(d["A_log"]), g)
     gdn.gdn_sigmoid(dev(d["b"][:, 0]), beta)
     v, z, x = dev(d["v"][:, 0]), dev(d["z"][:, 0]), dev(d["x"][:, 0])
     cw, nw = dev(d["conv_w"]), dev(d["norm_w"])
     wb = inputs.WORKLOADS[4]
     lb = inputs.draw_block_layer(0, wb, n_seqs=3)
-    b_in = {key: (_bits(val) if val.dtype == np.uint16 else dev(val)) for key, val in lb.items()}
+    b_in = upload_layer(lb)
     ws = torch.zeros(gdn.gdn_decode_block_workspace_bytes(3, HK, H), dtype=torch.uint8,
                      device=DEV)
 
@@ -63,10 +63,10 @@ def test_decode_step_graph_replays_equal_eager():
         gdn.gdn_recurrence(b["st"], q, k, v, g, beta, b["y"], w.scale)
         gdn.gdn_gated_rmsnorm(b["y"], nw, z, b["out"], w.eps)
         gdn.gdn_decode_block_bf16(b_in["qkv"], b_in["z"], b_in["a"], b_in["b"], b_in["conv_w"],
-                                  b_in["A_log"], b_in["dt_bias"], b_in["norm_w"], b["bcs"],
+                                  b_in["ssm_a"], b_in["dt_bias"], b_in["norm_w"], b["bcs"],
                                   b["bst"], b["bout"], HK, wb.scale, wb.l2_eps, wb.eps)
         gdn.gdn_decode_block_bf16_ex(b_in["qkv"], b_in["z"], b_in["a"], b_in["b"],
-                                     b_in["conv_w"], b_in["A_log"], b_in["dt_bias"],
+                                     b_in["conv_w"], b_in["ssm_a"], b_in["dt_bias"],
                                      b_in["norm_w"], b["scs"], b["sst"], b["sout"], ws, HK,
                                      wb.scale, wb.l2_eps, wb.eps)
 

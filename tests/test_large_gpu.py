@@ -26,7 +26,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import DEV, assert_close, host, oracle_threads
+from gpu_helpers import DEV, assert_close, dev_ssm_a, host, oracle_threads
 from linear_attention_ssm_recurrence_amd import gdn
 
 pytestmark = pytest.mark.gpu
@@ -97,7 +97,7 @@ def test_decode_step_state_past_2g_elements():
     st0 = {pr: host(state[pr]) for pr in pairs}
     y = torch.empty((N, H, S), device=DEV)
     scale = 1 / math.sqrt(S)
-    gdn.gdn_decode_step(state, q, k, v, a, b, A_log, dt_bias, y, scale)
+    gdn.gdn_decode_step(state, q, k, v, a, b, dev_ssm_a(A_log), dt_bias, y, scale)
     g_ref = oracle.decay_gate(host(a), host(dt_bias), host(A_log))
     b_ref = oracle.sigmoid(host(b))
     for n, h in pairs:
@@ -195,6 +195,7 @@ def test_decode_block_state_past_2g_elements(split):
     a, b = _randn((N, H), gen), _randn((N, H), gen)
     conv_w = _randn((C, K), gen, 0.5)
     A_log, dt_bias = _randn((H,), gen), torch.zeros(H, device=DEV)
+    ssm_a = dev_ssm_a(A_log)
     norm_w = 1 + _randn((S,), gen, 0.1)
     conv_state = _randn((N, C, K - 1), gen)
     state = _randn((N, H, S, S), gen, 0.05)
@@ -207,11 +208,11 @@ def test_decode_block_state_past_2g_elements(split):
     if split:
         ws = torch.zeros(gdn.gdn_decode_block_workspace_bytes(N, HK, H), dtype=torch.uint8,
                          device=DEV)
-        gdn.gdn_decode_block_bf16_ex(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state,
+        gdn.gdn_decode_block_bf16_ex(qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state,
                                      state, out, ws, HK, scale)
         assert int(ws.count_nonzero()) == 0, "split layer: workspace not zero after the call"
     else:
-        gdn.gdn_decode_block_bf16(qkv, z, a, b, conv_w, A_log, dt_bias, norm_w, conv_state,
+        gdn.gdn_decode_block_bf16(qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state,
                                   state, out, HK, scale)
     for n in seqs:
         d = before[n]

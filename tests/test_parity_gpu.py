@@ -18,7 +18,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import (ATOL, DEV, RTOL, RTOL_LONG_SCAN, assert_close, dev, dev_bits, host,
+from gpu_helpers import (ATOL, DEV, RTOL, RTOL_LONG_SCAN, assert_close, dev_ssm_a, dev, dev_bits, host,
                          oracle_threads, prep_recurrence, widen_bf16)
 from linear_attention_ssm_recurrence_amd import gdn, inputs
 
@@ -208,7 +208,7 @@ def test_decay_gate_and_sigmoid():
     dt = (rng.standard_normal(H) * 0.5).astype(np.float32)
     A_log = rng.standard_normal(H).astype(np.float32)
     g = torch.empty((97, H), dtype=torch.float32, device=DEV)
-    gdn.gdn_decay_gate(dev(a), dev(dt), dev(A_log), g)
+    gdn.gdn_decay_gate(dev(a), dev(dt), dev_ssm_a(A_log), g)
     gh = host(g)
     assert (gh <= 0).all() and np.isfinite(gh).all()
     assert_close(gh, oracle.decay_gate(a, dt, A_log), "decay gate")
@@ -219,6 +219,27 @@ def test_decay_gate_and_sigmoid():
     xd = dev(x)
     gdn.gdn_sigmoid(xd, xd)   # in place
     assert torch.equal(xd, y)
+
+
+def test_ssm_a():
+    """ssm_a = -exp(A_log) (the gate's per-head factor, which both Foundry
+    pages prepare on the host) against the float64 exponential, over the
+    range of A_log where exp stays finite in fp32, and its overflow to -inf;
+    the in-place form gives the same bits."""
+    rng = np.random.default_rng(43)
+    A_log = np.concatenate([rng.standard_normal(1000) * 4, np.linspace(-87.0, 88.5, 201),
+                            [0.0, -0.0, -1e30, 89.0, 1e30]]).astype(np.float32)
+    out = torch.empty(A_log.size, dtype=torch.float32, device=DEV)
+    src = dev(A_log)
+    gdn.gdn_ssm_a(src, out)
+    got = host(out)
+    with np.errstate(over="ignore"):
+        ref = -np.exp(A_log.astype(np.float64))
+    fin = np.abs(ref) < 3.4e38
+    assert_close(got[fin], ref[fin], "ssm_a", rtol=1e-6, atol=0.0)
+    assert (got[~fin] == -np.inf).all()
+    gdn.gdn_ssm_a(src, src)   # in place
+    assert torch.equal(src, out)
 
 
 @pytest.mark.parametrize("HK,H,D", [(16, 32, 128), (2, 2, 32), (3, 12, 96), (1, 4, 1024)])
@@ -261,7 +282,7 @@ def test_single_decode_one_seq_stages_and_chain():
     gdn.gdn_l2norm_gqa(dev(d["q_raw"]), qg, w.l2_eps)
     assert_close(host(qg), p["q"], "one-sequence q l2norm+gqa")
     g = torch.empty((1, 1, H), dtype=torch.float32, device=DEV)
-    gdn.gdn_decay_gate(dev(d["a"]), dev(d["dt_bias"]), dev(d["A_log"]), g)
+    gdn.gdn_decay_gate(dev(d["a"]), dev(d["dt_bias"]), dev_ssm_a(d["A_log"]), g)
     assert_close(host(g), p["g"], "one-sequence gate")
     bt = torch.empty((1, 1, H), dtype=torch.float32, device=DEV)
     gdn.gdn_sigmoid(dev(d["b"]), bt)
@@ -301,7 +322,7 @@ def test_single_decode_one_seq_stages_and_chain():
     gdn.gdn_l2norm_gqa(co[:, kd:2 * kd].reshape(1, HK, S).contiguous(), kdv, w.l2_eps)
     gdd = torch.empty((1, H), dtype=torch.float32, device=DEV)
     bdd = torch.empty((1, H), dtype=torch.float32, device=DEV)
-    gdn.gdn_decay_gate(dev(d["a"][:, 0]), dev(d["dt_bias"]), dev(d["A_log"]), gdd)
+    gdn.gdn_decay_gate(dev(d["a"][:, 0]), dev(d["dt_bias"]), dev_ssm_a(d["A_log"]), gdd)
     gdn.gdn_sigmoid(dev(d["b"][:, 0]), bdd)
     stc = dev(d["state"])
     yc = torch.empty((1, H, S), dtype=torch.float32, device=DEV)
@@ -322,7 +343,7 @@ def _block_gpu(d, HK, scale, eps=1e-6):
     cs, st = dev(d["conv_state"]), dev(d["state"])
     out = torch.empty((N, H, S), dtype=torch.float32, device=DEV)
     gdn.gdn_decode_block_bf16(dev_bits(d["qkv"]), dev_bits(d["z"]), dev(d["a"]), dev(d["b"]),
-                              dev(d["conv_w"]), dev(d["A_log"]), dev(d["dt_bias"]),
+                              dev(d["conv_w"]), dev_ssm_a(d["A_log"]), dev(d["dt_bias"]),
                               dev(d["norm_w"]), cs, st, out, HK, scale, eps, eps)
     return out, cs, st
 
@@ -341,7 +362,7 @@ def _block_staged_gpu(d, HK, scale, eps=1e-6):
     gdn.gdn_l2norm_gqa(co[:, kd:2 * kd].reshape(N, HK, S).contiguous(), k, eps)
     g = torch.empty((N, H), dtype=torch.float32, device=DEV)
     b = torch.empty((N, H), dtype=torch.float32, device=DEV)
-    gdn.gdn_decay_gate(dev(d["a"]), dev(d["dt_bias"]), dev(d["A_log"]), g)
+    gdn.gdn_decay_gate(dev(d["a"]), dev(d["dt_bias"]), dev_ssm_a(d["A_log"]), g)
     gdn.gdn_sigmoid(dev(d["b"]), b)
     y = torch.empty((N, H, S), dtype=torch.float32, device=DEV)
     gdn.gdn_recurrence(st, q, k, co[:, 2 * kd:].reshape(N, H, S).contiguous(), g, b, y, scale)

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import DEV, RTOL_LONG_SCAN, assert_close, dev, dev_bits, host, oracle_threads
+from gpu_helpers import DEV, RTOL_LONG_SCAN, assert_close, dev_ssm_a, dev, dev_bits, host, oracle_threads
 from linear_attention_ssm_recurrence_amd import gdn, inputs
 
 pytestmark = pytest.mark.gpu
@@ -31,7 +31,7 @@ def _gpu_prefill(d, HK, scale, eps=1e-6, scan=None):
     out = torch.empty((N, T, H, S), device=DEV)
     ws = torch.empty(gdn.gdn_prefill_workspace_bytes(N, T, HK, H, S), dtype=torch.uint8, device=DEV)
     gdn.gdn_prefill_bf16(dev_bits(d["qkv"]), dev_bits(d["z"]), dev(d["a"]), dev(d["b"]),
-                         dev(d["conv_w"]), dev(d["A_log"]), dev(d["dt_bias"]), dev(d["norm_w"]),
+                         dev(d["conv_w"]), dev_ssm_a(d["A_log"]), dev(d["dt_bias"]), dev(d["norm_w"]),
                          cs, st, out, ws, HK, scale, eps, eps, scan=scan)
     return out, cs, st
 
@@ -68,7 +68,7 @@ def test_prefill_equals_decode_layers():
         gdn.gdn_decode_block_bf16(dev_bits(np.ascontiguousarray(d["qkv"][:, t])),
                                   dev_bits(np.ascontiguousarray(d["z"][:, t])),
                                   dev(d["a"][:, t]), dev(d["b"][:, t]), dev(d["conv_w"]),
-                                  dev(d["A_log"]), dev(d["dt_bias"]), dev(d["norm_w"]), cs2, st2,
+                                  dev_ssm_a(d["A_log"]), dev(d["dt_bias"]), dev(d["norm_w"]), cs2, st2,
                                   o, HK, scale, 1e-6, 1e-6)
         assert torch.equal(o, out[:, t]), f"position {t}: prefill != decode layer"
     assert torch.equal(st2, st) and torch.equal(cs2, cs)

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import DEV, assert_close, dev, dev_bits, host, oracle_threads
+from gpu_helpers import DEV, assert_close, dev_ssm_a, dev, dev_bits, host, oracle_threads
 from linear_attention_ssm_recurrence_amd import gdn, inputs
 
 pytestmark = pytest.mark.gpu
@@ -152,7 +152,7 @@ def test_random_prefill(case):
     ws = torch.empty(gdn.gdn_prefill_workspace_bytes(N, T, HK, H, 128), dtype=torch.uint8,
                      device=DEV)
     gdn.gdn_prefill_bf16(dev_bits(d["qkv"]), dev_bits(d["z"]), dev(d["a"]), dev(d["b"]),
-                         dev(d["conv_w"]), dev(d["A_log"]), dev(d["dt_bias"]), dev(d["norm_w"]),
+                         dev(d["conv_w"]), dev_ssm_a(d["A_log"]), dev(d["dt_bias"]), dev(d["norm_w"]),
                          cs, st, out, ws, HK, scale, scan=scan)
     what = f"prefill N={N} T={T} HK={HK} H={H} K={K} scan={scan}"
     assert_close(host(out), o_ref, what + " out")
@@ -209,7 +209,7 @@ def test_random_decode_layer(case):
     o_ref, cs_ref, st_ref = oracle.decode_block_bf16(
         d["qkv"], d["z"], d["a"], d["b"], d["conv_w"], d["A_log"], d["dt_bias"], d["norm_w"],
         d["conv_state"], d["state"], HK, scale)
-    fixed = [dev(d[k]) for k in ("conv_w", "A_log", "dt_bias", "norm_w")]
+    fixed = [dev(d["conv_w"]), dev_ssm_a(d["A_log"]), dev(d["dt_bias"]), dev(d["norm_w"])]
     step = [dev_bits(d["qkv"]), dev_bits(d["z"]), dev(d["a"]), dev(d["b"])]
     ws = torch.zeros(gdn.gdn_decode_block_workspace_bytes(N, HK, H), dtype=torch.uint8, device=DEV)
     results = []

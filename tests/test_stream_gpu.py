@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import DEV, dev, prep_recurrence
+from gpu_helpers import DEV, dev, prep_recurrence, upload_layer
 from linear_attention_ssm_recurrence_amd import gdn, inputs
 
 pytestmark = pytest.mark.gpu
@@ -37,13 +37,13 @@ def test_side_stream_equals_default_stream():
     def run(stream):
         st_scan = dev(p["state"])
         y_scan = torch.empty(p["v"].shape, device=DEV)
-        b_in = {key: (_bits(val) if val.dtype == np.uint16 else dev(val)) for key, val in lb.items()}
+        b_in = upload_layer(lb)
         out = torch.empty((4, H, S), device=DEV)
         with torch.cuda.stream(stream):
             gdn.gdn_recurrence_seq(st_scan, dev(p["q"]), dev(p["k"]), dev(p["v"]), dev(p["g"]),
                                    dev(p["beta"]), y_scan, w.scale)
             gdn.gdn_decode_block_bf16(b_in["qkv"], b_in["z"], b_in["a"], b_in["b"],
-                                      b_in["conv_w"], b_in["A_log"], b_in["dt_bias"],
+                                      b_in["conv_w"], b_in["ssm_a"], b_in["dt_bias"],
                                       b_in["norm_w"], b_in["conv_state"], b_in["state"], out, HK,
                                       wb.scale, wb.l2_eps, wb.eps)
         stream.synchronize()
@@ -71,10 +71,10 @@ def test_split_layer_on_two_streams_with_own_workspaces():
     layers = [inputs.draw_block_layer(l, wb, n_seqs=n) for l, n in ((2, 24), (3, 40))]
 
     def upload(lb):
-        return {key: (_bits(val) if val.dtype == np.uint16 else dev(val)) for key, val in lb.items()}
+        return upload_layer(lb)
 
     def call(fn, t, out, *extra):
-        fn(t["qkv"], t["z"], t["a"], t["b"], t["conv_w"], t["A_log"], t["dt_bias"], t["norm_w"],
+        fn(t["qkv"], t["z"], t["a"], t["b"], t["conv_w"], t["ssm_a"], t["dt_bias"], t["norm_w"],
            t["conv_state"], t["state"], out, *extra, HK, wb.scale, wb.l2_eps, wb.eps)
 
     ref, got, wss = [], [], []
