@@ -74,15 +74,17 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--legs",
                     default="decode,scan,block,decode_full,decode_t4,spec,prefill,single,machine")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--cpu-runs", type=int, default=5,
+                    help="timed runs of each oracle baseline (after one warm-up); the median "
+                         "is reported")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run a plain 512 MiB device copy three times (a known-size "
-                         "kernel for scaling hardware byte counters)")
+                    help="also run a plain 512 MiB device copy and a 512 MiB fill three times "
+                         "each (known-size kernels for scaling hardware byte counters, and the "
+                         "write-only rate)")
     return ap.parse_args()
 
 
@@ -198,16 +200,25 @@ def run_decode(torch, gdn, inputs, steps, warmup, with_glue=False, t4=False, fus
 
     for i in range(warmup):
         step(i)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     with Timer(torch) as tm:
         for i in range(steps):
+            if i:
+                marks[i - 1].record()
             step(i)
+        marks[-1].record()
     b = decode_bytes(w)
     ms_wall = tm.wall_ms / steps
     ms_ev = tm.event_ms / steps
+    # per launch: from the previous launch's end mark (the timed region's start for
+    # the first) to its own; the launches run back to back
+    bounds = [tm.ev0] + marks
+    per_launch = sorted(a.elapsed_time(c) for a, c in zip(bounds[:-1], bounds[1:]))
     res = {
         "workload": "batched decode: 256 sequences x 32 V-heads x S=128, fp32 state 512 MiB",
         "ms_per_step": ms_wall,
         "kernel_ms_events": ms_ev,
+        "kernel_ms_median": per_launch[len(per_launch) // 2],
         "state_GBps": b["state"] / (ms_wall * 1e-3) / 1e9,
         "total_GBps": b["total"] / (ms_wall * 1e-3) / 1e9,
         "algorithmic_bytes_per_launch": b["total"],
@@ -279,7 +290,7 @@ def run_scan(torch, gdn, inputs, steps, warmup):
     ms = t_all.wall_ms / steps
     scan_ms = t_scan.event_ms / steps
     conv_ms = t_conv.event_ms / steps
-    flops = 7.0 * N * T * H * S * S        # 1 mul + 3 fma per state element and token
+    flops = scan_method_flops(N, T, H, S)
     conv_bytes = 2 * N * T * C * 4 + C * w.conv_kernel * 4 + 2 * N * C * (w.conv_kernel - 1) * 4
     scan_bytes = (4 * N * T * H * S + 2 * N * T * H) * 4 + 2 * N * H * S * S * 4
     return {
@@ -296,9 +307,17 @@ def run_scan(torch, gdn, inputs, steps, warmup):
         "scan_t4_kernel_ms": t_t4.event_ms / steps,
         "chunked_scan_ms": t_chunk.event_ms / steps,
         "chunked_scan_tokens_per_s": N * T / (t_chunk.event_ms / steps * 1e-3),
+        "chunked_method_TFLOPs": flops / (t_chunk.event_ms / steps * 1e-3) / 1e12,
+        "chunked_frac_method_flops": flops / (t_chunk.event_ms / steps * 1e-3) / 1e12
+                                     / FP32_MFMA_PEAK_TFLOPS,
+        "chunked_frac_method_flops_note": "the method's own 7 flop per state element and token "
+                                          "over the fp32 matrix peak",
         "chunked_mfma_TFLOPs": chunked_mfma_flops(N, T, H, q.shape[2]) / (t_chunk.event_ms / steps * 1e-3) / 1e12,
-        "chunked_frac_fp32_mfma_peak": chunked_mfma_flops(N, T, H, q.shape[2]) / (t_chunk.event_ms / steps * 1e-3)
-                                       / 1e12 / FP32_MFMA_PEAK_TFLOPS,
+        "chunked_mfma_pipe_frac": chunked_mfma_flops(N, T, H, q.shape[2]) / (t_chunk.event_ms / steps * 1e-3)
+                                  / 1e12 / FP32_MFMA_PEAK_TFLOPS,
+        "chunked_mfma_pipe_frac_note": "matrix-pipe utilisation: the MFMA work the chunked form "
+                                       "executes (1.34x the method's flops: masked Gram tiles, "
+                                       "the blockwise inverse) over the same peak",
         "conv_kernel_ms": conv_ms,
         "conv_GBps": conv_bytes / (conv_ms * 1e-3) / 1e9,
         "conv_frac_hbm_peak": conv_bytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -308,6 +327,14 @@ def run_scan(torch, gdn, inputs, steps, warmup):
 def w_scan_tokens(leg) -> float:
     """Tokens per step of the scan leg (conv + scan over one 4096-token sequence)."""
     return leg["tokens_per_s"] * leg["ms_per_step"] * 1e-3
+
+
+def scan_method_flops(N, T, H, S) -> float:
+    """The method's own arithmetic over a scan: per state element and token,
+    the decay (1 mul) and three multiply-adds (the prediction, the rank-1
+    update, the read-out), 7 flop; the same count for the sequential and
+    the chunked form."""
+    return 7.0 * N * T * H * S * S
 
 
 def chunked_mfma_flops(N, T, H, HK=None) -> float:
@@ -643,53 +670,138 @@ def recorded_traffic():
     return int(fields["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(inputs, d, budget_s):
-    """The C oracle's decode recurrence on a sample of the headline batch, on
-    this host's cores. The oracle routine is called directly on arrays
-    prepared once (the test front end's defensive copies are not timed)."""
+def _median_seconds(run, runs):
+    """Median wall time of `runs` calls of run() after one untimed warm-up."""
+    run()
+    times = []
+    for _ in range(max(1, runs)):
+        t0 = time.perf_counter()
+        run()
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times))
+
+
+def cpu_baseline(inputs, d, runs):
+    """The C oracle timed on this host's cores, in the GPU legs' units, each
+    figure the median of `runs` timed runs after a warm-up, on all host
+    threads (OpenMP over independent rows) and on one:
+      decode  the headline batch, all 256 sequences (512 MiB of state, far
+              beyond the host's caches): state GB/s, 10 steps per run on all
+              threads, one step per run on one thread;
+      scan    the scan workload (one sequence, 32 heads, S = 128) over its
+              first 512 of 4096 tokens (a scan's cost per token is the same at
+              every position): tokens/s;
+      block   the fused bf16 layer on 64 sequences, two distinct layers of the
+              48-layer workload per run: ms per 48-layer step (48 x the
+              median time per layer).
+    The oracle routines are called directly on arrays prepared once (the
+    test front end's defensive copies are not timed)."""
     import ctypes
     import oracle
     threads = host_threads()
-    oracle.set_threads(threads)
     lib = oracle._lib("f32")
-    w = inputs.WORKLOADS[2]
-    n, H, S = 32, w.n_v_heads, w.state_size
     f32 = lambda x: np.ascontiguousarray(x, dtype=np.float32)
-    q = f32(oracle.l2norm_gqa(d["q_raw"][:n], H, w.l2_eps))
-    k = f32(oracle.l2norm_gqa(d["k_raw"][:n], H, w.l2_eps))
-    g = f32(oracle.decay_gate(d["a"][:n], d["dt_bias"], d["A_log"]))
-    beta = f32(oracle.sigmoid(d["b"][:n]))
-    v = f32(d["v"][:n])
-    st = f32(d["state"][:n]).copy()
-    y = np.empty_like(v)
     P = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    out = {}
 
-    def run():
-        lib.oracle_recurrence_seq(P(st), P(q), P(k), P(v), P(g), P(beta), P(y), n, 1, H, S,
-                                  float(w.scale))
+    def both(name, make_run, per_run_multi, per_run_single):
+        res = {}
+        for label, nthreads, per_run in (("all", threads, per_run_multi),
+                                         ("one", 1, per_run_single)):
+            oracle.set_threads(nthreads)
+            res[label] = (_median_seconds(make_run(per_run), runs), per_run)
+        oracle.set_threads(threads)
+        log(f"cpu baseline {name}: {res}")
+        return res
 
-    def timed(budget):
-        run()                                          # warm-up
-        reps, t0 = 0, time.perf_counter()
-        while True:
-            run()
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= budget or reps >= 10000:
-                return reps, el
+    # decode: all 256 sequences of the headline batch
+    w = inputs.WORKLOADS[2]
+    n, H, S = w.n_seqs, w.n_v_heads, w.state_size
+    q = f32(oracle.l2norm_gqa(d["q_raw"], H, w.l2_eps))
+    k = f32(oracle.l2norm_gqa(d["k_raw"], H, w.l2_eps))
+    g = f32(oracle.decay_gate(d["a"], d["dt_bias"], d["A_log"]))
+    beta = f32(oracle.sigmoid(d["b"]))
+    v = f32(d["v"])
+    st = f32(d["state"]).copy()
+    y = np.empty_like(v)
 
+    def decode_run(steps):
+        def run():
+            for _ in range(steps):
+                lib.oracle_recurrence_seq(P(st), P(q), P(k), P(v), P(g), P(beta), P(y), n, 1, H,
+                                          S, float(w.scale))
+        return run
+
+    r = both("decode", decode_run, 10, 1)
     state_bytes = 2 * n * H * S * S * 4
-    reps, el = timed(budget_s)
-    oracle.set_threads(1)
-    reps1, el1 = timed(max(1.0, budget_s / 4))
-    oracle.set_threads(threads)
-    return {"value": state_bytes * reps / el / 1e9, "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{n} of the 256 sequences (all 32 V-heads, S=128): {reps} decode steps "
-                      f"in {el:.1f} s; state bytes read+written per second",
-            "single_thread_value": state_bytes * reps1 / el1 / 1e9,
-            "single_thread_sample": f"the same {n} sequences on 1 thread: {reps1} decode steps "
-                                    f"in {el1:.1f} s"}
+    dec = {lab: state_bytes * steps / sec / 1e9 for lab, (sec, steps) in r.items()}
+    del q, k, v, st, y
+
+    # scan: the first 512 tokens of the scan workload, all 32 heads
+    ws = inputs.WORKLOADS[3]
+    dsc = inputs.draw(ws)
+    Tn = 512
+    Hs, Ss = ws.n_v_heads, ws.state_size
+    sq = f32(oracle.l2norm_gqa(dsc["q_raw"][:, :Tn], Hs, ws.l2_eps))
+    sk = f32(oracle.l2norm_gqa(dsc["k_raw"][:, :Tn], Hs, ws.l2_eps))
+    sg = f32(oracle.decay_gate(dsc["a"][:, :Tn], dsc["dt_bias"], dsc["A_log"]))
+    sb = f32(oracle.sigmoid(dsc["b"][:, :Tn]))
+    sv = f32(dsc["v"][:, :Tn])
+    sy = np.empty_like(sv)
+    s0 = f32(dsc["state"])
+    sst = s0.copy()
+
+    def scan_run(_):
+        def run():
+            sst[...] = s0
+            lib.oracle_recurrence_seq(P(sst), P(sq), P(sk), P(sv), P(sg), P(sb), P(sy), 1, Tn, Hs,
+                                      Ss, float(ws.scale))
+        return run
+
+    r = both("scan", scan_run, 1, 1)
+    scan = {lab: Tn / sec for lab, (sec, _) in r.items()}
+    del dsc, sq, sk, sv, sy
+
+    # block: two layers of the 64-sequence, 48-layer bf16 workload
+    wb = inputs.WORKLOADS[4]
+    layers = []
+    for l in (0, 1):
+        lb = inputs.draw_block_layer(l, wb)
+        t = {key: (np.ascontiguousarray(val) if val.dtype == np.uint16 else f32(val))
+             for key, val in lb.items()}
+        t["out"] = np.empty((wb.n_seqs, wb.n_v_heads, wb.state_size), dtype=np.float32)
+        layers.append(t)
+
+    def block_run(_):
+        def run():
+            for t in layers:
+                lib.oracle_decode_block_bf16(
+                    P(t["qkv"]), P(t["z"]), P(t["a"]), P(t["b"]), P(t["conv_w"]), P(t["A_log"]),
+                    P(t["dt_bias"]), P(t["norm_w"]), P(t["conv_state"]), P(t["state"]),
+                    P(t["out"]), wb.n_seqs, wb.n_k_heads, wb.n_v_heads, wb.state_size,
+                    wb.conv_kernel, float(wb.scale), float(wb.l2_eps), float(wb.eps))
+        return run
+
+    r = both("block", block_run, 1, 1)
+    block = {lab: sec / len(layers) * wb.layers * 1e3 for lab, (sec, _) in r.items()}
+    out = {"value": dec["all"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": (f"the decode step of all 256 sequences (all 32 V-heads, S=128, 512 MiB "
+                      f"of state): state bytes read+written per second, median of {runs} runs "
+                      f"of 10 steps after a warm-up, on {threads} threads"),
+           "single_thread_value": dec["one"],
+           "single_thread_sample": f"the same, one step per run, on 1 thread",
+           "scan": {"value": scan["all"], "unit": "tokens/s", "cores": threads,
+                    "single_thread_value": scan["one"],
+                    "sample": (f"the sequential scan over the first {Tn} of the 4096 tokens of "
+                               f"the scan workload (1 sequence, 32 heads, S=128, from a zero "
+                               f"state), median of {runs} runs after a warm-up")},
+           "block": {"value": block["all"], "unit": "ms per 48-layer step", "cores": threads,
+                     "single_thread_value": block["one"],
+                     "sample": (f"the fused bf16 decode layer on 64 sequences (16 -> 32 heads, "
+                                f"S=128, C=8192, K=4), layers 0 and 1 of the workload per run; "
+                                f"48 x the median time per layer over {runs} runs after a "
+                                f"warm-up")}}
+    return out
 
 
 def main():
@@ -754,7 +866,7 @@ def main():
         torch.cuda.empty_cache()
 
     if args.calibrate_copy:
-        log("copy calibration: 3 x 512 MiB device-to-device copy")
+        log("copy calibration: 3 x 512 MiB device-to-device copy, 3 x 512 MiB fill")
         src = torch.ones(128 * 1024 * 1024, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
@@ -762,8 +874,15 @@ def main():
         with Timer(torch) as tc:
             for _ in range(3):
                 dst.copy_(src)
+        for _ in range(3):
+            dst.fill_(1.0)
+        with Timer(torch) as tf:
+            for _ in range(3):
+                dst.fill_(1.0)
         line_copy = {"bytes_read_per_copy": src.numel() * 4, "bytes_written_per_copy": src.numel() * 4,
-                     "GBps": 2 * src.numel() * 4 * 3 / (tc.event_ms * 1e-3) / 1e9}
+                     "GBps": 2 * src.numel() * 4 * 3 / (tc.event_ms * 1e-3) / 1e9,
+                     "fill_bytes_written": dst.numel() * 4,
+                     "fill_GBps": dst.numel() * 4 * 3 / (tf.event_ms * 1e-3) / 1e9}
         del src, dst
     achieved = dec["algorithmic_bytes_per_launch"] / (dec["kernel_ms_events"] * 1e-3) / 1e9
     line = {
@@ -788,6 +907,7 @@ def main():
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "kernel_ms": dec["kernel_ms_events"],
+                     "kernel_ms_median": dec["kernel_ms_median"],
                      "bytes_per_launch": dec["algorithmic_bytes_per_launch"],
                      "traffic": recorded_traffic()},
         "legs": out_legs,
@@ -801,8 +921,8 @@ def main():
         line["scan_sequential_tokens_per_s"] = (
             w_scan_tokens(out_legs["scan"]) / (out_legs["scan"]["sequential_ms_per_step"] * 1e-3))
     if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle on {host_threads()} threads, ~{args.cpu_seconds:.0f} s")
-        line["cpu_baseline"] = cpu_baseline(inputs, d, args.cpu_seconds)
+        log(f"cpu baseline: oracle on {host_threads()} threads and on 1")
+        line["cpu_baseline"] = cpu_baseline(inputs, d, args.cpu_runs)
     print(json.dumps(line), flush=True)
 
 

@@ -47,6 +47,17 @@ def test_chunked_mfma_flops_match_the_counted_instructions():
     assert flops == 2048.0 * (256 * 4 * 128 * 64 + 2048 * 704)
 
 
+def test_scan_method_flops():
+    """The scan workload's own work, 1 sequence x 4096 tokens x 32 heads x
+    S = 128 = 2,147,483,648 element-tokens at 7 flop: 1.503e10 flop. The
+    chunked form executes 1.34 times as much on the matrix pipes (the
+    fraction reported as the chunked scan's roofline uses this count)."""
+    b = _bench()
+    f = b.scan_method_flops(1, 4096, 32, 128)
+    assert f == 7 * 2_147_483_648 == 15_032_385_536
+    assert 1.33 < b.chunked_mfma_flops(1, 4096, 32) / f < 1.35
+
+
 def test_bench_refuses_more_than_one_gpu():
     run = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                          capture_output=True, text=True, timeout=120)
