@@ -321,6 +321,32 @@ int gdn_decode_block_bf16_ex(const uint16_t *qkv, const uint16_t *z, const float
                              int n_seqs, int n_k_heads, int n_v_heads, int state_size,
                              int conv_kernel, float scale, float l2_eps, float eps, void *stream);
 
+/* Capacity of the library-owned counter array of gdn_decode_block_bf16_noalloc,
+   per GPU: n_seqs * (n_k_heads + n_v_heads) may not exceed it. */
+#define GDN_NOALLOC_MAX_COUNTERS 65536
+
+/*
+ * gdn_decode_block_bf16_ex without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Same steps, arguments (but the
+ * workspace) and results, bit for bit. Its counters live in a library-owned
+ * device array of GDN_NOALLOC_MAX_COUNTERS 32-bit counters (256 KiB) on each
+ * GPU it runs on, held until the process ends; the call itself allocates
+ * nothing. The array starts zero and every completed call leaves it zero.
+ * Calls that overlap on one GPU (on different streams, or from several host
+ * threads) share the array and race: the caller serialises them, or uses
+ * gdn_decode_block_bf16_ex with a workspace of its own per stream.
+ * Errors: as gdn_decode_block_bf16; GDN_ESIZE also when n_seqs * (n_k_heads +
+ * n_v_heads) > GDN_NOALLOC_MAX_COUNTERS; GDN_ELAUNCH also when the array's
+ * device address cannot be found (no usable GPU).
+ */
+int gdn_decode_block_bf16_noalloc(const uint16_t *qkv, const uint16_t *z, const float *a,
+                                  const float *b, const float *conv_w, const float *ssm_a,
+                                  const float *dt_bias, const float *norm_w, float *conv_state,
+                                  float *state, float *out, int n_seqs, int n_k_heads,
+                                  int n_v_heads, int state_size, int conv_kernel, float scale,
+                                  float l2_eps, float eps, void *stream);
+
 /*
  * Workspace, in bytes, that gdn_prefill_bf16 and gdn_prefill_bf16_ex (either
  * scan) need for these sizes (0 for invalid sizes): normalised q and k per

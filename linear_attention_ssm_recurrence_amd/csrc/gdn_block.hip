@@ -28,6 +28,7 @@
 // step, so the layer equals the stand-alone kernels chained, bit for bit.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
+#include <mutex>
 
 namespace gdn {
 
@@ -635,4 +636,69 @@ extern "C" int gdn_decode_block_bf16_ex(const uint16_t* qkv, const uint16_t* z, 
   return dispatch_block_split(qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state, state,
                               out, static_cast<unsigned*>(workspace), n_seqs, n_k_heads,
                               n_v_heads, conv_kernel, scale, l2_eps, eps, as_stream(stream));
+}
+
+// ---------------------------------------------------------------------------
+// The split layer without a workspace argument (gdn_decode_block_bf16_noalloc),
+// for callers that cannot allocate device memory. Its counters live in a
+// library-owned device array, one per GPU, of GDN_NOALLOC_MAX_COUNTERS 32-bit
+// counters (256 KiB), held until the process ends. The array has no
+// initialiser, so it starts zero on every device, and every completed call
+// leaves the counters it used zero again (the split kernel's last arrivers
+// reset them), so no call needs to clear it. Calls that overlap on one GPU
+// share the array and race.
+// ---------------------------------------------------------------------------
+namespace gdn {
+
+constexpr int64_t kNoAllocCounters = GDN_NOALLOC_MAX_COUNTERS;
+static_assert(kNoAllocCounters * sizeof(unsigned) <= 256 * 1024, "a modest scratch array");
+
+__device__ __align__(256) unsigned scratch[kNoAllocCounters];
+
+// Device address of the current GPU's copy of `scratch`, looked up once per
+// device with that device current. In host code the array's name is only a
+// host-side stand-in: a kernel must be given this address, never the name.
+static int scratch_address(unsigned** out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<unsigned*> addr[kMaxDevices];
+  static std::mutex mu;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GDN_ELAUNCH;
+  unsigned* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* sym = nullptr;
+      if (hipGetSymbolAddress(&sym, HIP_SYMBOL(scratch)) != hipSuccess || !sym) return GDN_ELAUNCH;
+      p = static_cast<unsigned*>(sym);
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return GDN_OK;
+}
+
+}  // namespace gdn
+
+extern "C" int gdn_decode_block_bf16_noalloc(const uint16_t* qkv, const uint16_t* z,
+                                             const float* a, const float* b,
+                                             const float* conv_w, const float* ssm_a,
+                                             const float* dt_bias, const float* norm_w,
+                                             float* conv_state, float* state, float* out,
+                                             int n_seqs, int n_k_heads, int n_v_heads,
+                                             int state_size, int conv_kernel, float scale,
+                                             float l2_eps, float eps, void* stream) {
+  int64_t count = 0;
+  const int rc = check_block_split(qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state,
+                                   state, out, n_seqs, n_k_heads, n_v_heads, state_size,
+                                   conv_kernel, &count);
+  if (rc != GDN_OK) return finish_check(rc);
+  if (count > kNoAllocCounters) return GDN_ESIZE;
+  unsigned* counters = nullptr;
+  const int src = scratch_address(&counters);
+  if (src != GDN_OK) return src;
+  return dispatch_block_split(qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state, state,
+                              out, counters, n_seqs, n_k_heads, n_v_heads, conv_kernel, scale,
+                              l2_eps, eps, as_stream(stream));
 }

@@ -29,6 +29,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "gdn.h")
 GDN_OK, GDN_ENULL, GDN_ESIZE, GDN_EUNSUPPORTED, GDN_EALIGN, GDN_ELAUNCH = range(6)
 GDN_RECUR_EXACT, GDN_RECUR_T4 = 0, 1
 GDN_SCAN_SEQUENTIAL, GDN_SCAN_CHUNKED = 0, 1
+GDN_NOALLOC_MAX_COUNTERS = 65536
 
 
 class GdnError(RuntimeError):
@@ -65,6 +66,7 @@ def load_library():
         "gdn_gated_rmsnorm": [P, P, P, P, L, I, F, P],
         "gdn_decode_block_bf16": [P] * 11 + [I] * 5 + [F] * 3 + [P],
         "gdn_decode_block_bf16_ex": [P] * 12 + [ctypes.c_size_t] + [I] * 5 + [F] * 3 + [P],
+        "gdn_decode_block_bf16_noalloc": [P] * 11 + [I] * 5 + [F] * 3 + [P],
         "gdn_prefill_bf16": [P] * 12 + [ctypes.c_size_t] + [I] * 6 + [F] * 3 + [P],
         "gdn_prefill_bf16_ex": [P] * 12 + [ctypes.c_size_t] + [I] * 6 + [F] * 3 + [I, P],
         "gdn_recurrence_seq_chunked": [P] * 8 + [ctypes.c_size_t] + [I] * 5 + [F, P],
@@ -362,6 +364,24 @@ def gdn_decode_block_bf16(qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_sta
 
 def gdn_decode_block_workspace_bytes(n_seqs, n_k_heads, n_v_heads) -> int:
     return int(load_library().gdn_decode_block_workspace_bytes(n_seqs, n_k_heads, n_v_heads))
+
+
+@_typed
+def gdn_decode_block_bf16_noalloc(qkv, z, a, b, conv_w, ssm_a, dt_bias, norm_w, conv_state,
+                                  state, out, n_k_heads, scale, l2_eps=1e-6, eps=1e-6,
+                                  stream=None):
+    """gdn_decode_block_bf16_ex without a workspace: the counters live in the
+    library's own per-GPU array (n_seqs * (HK + H) <= GDN_NOALLOC_MAX_COUNTERS);
+    calls that overlap on one GPU race."""
+    N, H, S = z.shape
+    C, K = conv_w.shape
+    _block_shapes(qkv, a, b, ssm_a, dt_bias, norm_w, conv_state, state, out, N, H, S, C, K,
+                  n_k_heads)
+    _call("gdn_decode_block_bf16_noalloc", _ptr16(qkv, "qkv"), _ptr16(z, "z"),
+          _ptr(a, F32, "a"), _ptr(b, F32, "b"), _ptr(conv_w, F32, "conv_w"),
+          _ptr(ssm_a, F32, "ssm_a"), _ptr(dt_bias, F32, "dt_bias"), _ptr(norm_w, F32, "norm_w"),
+          _ptr(conv_state, F32, "conv_state"), _ptr(state, F32, "state"), _ptr(out, F32, "out"),
+          N, n_k_heads, H, S, K, float(scale), float(l2_eps), float(eps), _stream(z, stream))
 
 
 @_typed

@@ -119,6 +119,12 @@ int main(void) {
                                     NULL),
          GDN_EUNSUPPORTED);
 
+  EXPECT(gdn_decode_block_bf16_noalloc(buf16, buf16, cf, cf, cf, cf, cf, cf, f, f, f, 1366, 16, 32,
+                                       128, 4, 0.1f, 1e-6f, 1e-6f, NULL),
+         GDN_ESIZE); /* 1366 * 48 counters > GDN_NOALLOC_MAX_COUNTERS */
+  EXPECT(gdn_decode_block_bf16_noalloc(NULL, buf16, cf, cf, cf, cf, cf, cf, f, f, f, 3, 16, 32,
+                                       128, 4, 0.1f, 1e-6f, 1e-6f, NULL),
+         GDN_ENULL);
   EXPECT(gdn_ssm_a(NULL, f, 4, NULL), GDN_ENULL);
   EXPECT(gdn_ssm_a(cf, NULL, 4, NULL), GDN_ENULL);
   EXPECT(gdn_ssm_a(cf, f, -1, NULL), GDN_ESIZE);

@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_header_symbol(lib):
     names = gdn.header_symbols()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     out = os.popen(f"nm -D --defined-only {gdn.LIB_PATH}").read()
     exported = set(re.findall(r"\sT\s(gdn_\w+)", out))
     for name in names:
@@ -184,6 +184,31 @@ def test_block_validation(lib):
     assert call(HK=0) == gdn.GDN_ESIZE
     assert call(HK=12) == gdn.GDN_ESIZE                 # 32 % 12 != 0
     assert call(HK=4) == gdn.GDN_EUNSUPPORTED           # 8 V-heads per K-head
+    assert call(S=64) == gdn.GDN_EUNSUPPORTED
+    assert call(K=5) == gdn.GDN_EUNSUPPORTED
+    assert call(state=FAKE_MIS) == gdn.GDN_EALIGN
+    assert call(z=ctypes.c_void_p(0x10002)) == gdn.GDN_EALIGN
+    assert call(first=NUL, state=NUL, n=0) == gdn.GDN_OK
+
+
+def test_block_noalloc_validation(lib):
+    """The allocation-free split layer checks its arguments as the workspace
+    form does, and refuses with GDN_ESIZE a batch whose counters
+    (n_seqs * (n_k_heads + n_v_heads)) exceed its array, before it looks up
+    the array or launches anything."""
+    f = lib.gdn_decode_block_bf16_noalloc
+
+    def call(first=FAKE, state=FAKE, n=3, HK=16, H=32, S=128, K=4, z=FAKE):
+        return f(first, z, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, state, FAKE,
+                 n, HK, H, S, K, 0.1, 1e-6, 1e-6, NUL)
+
+    cap = gdn.GDN_NOALLOC_MAX_COUNTERS
+    assert cap == 65536
+    assert call(n=cap // 48 + 1) == gdn.GDN_ESIZE       # 1366 x (16 + 32) > 65536
+    assert call(first=NUL) == gdn.GDN_ENULL
+    assert call(n=-1) == gdn.GDN_ESIZE
+    assert call(HK=12) == gdn.GDN_ESIZE
+    assert call(HK=4) == gdn.GDN_EUNSUPPORTED
     assert call(S=64) == gdn.GDN_EUNSUPPORTED
     assert call(K=5) == gdn.GDN_EUNSUPPORTED
     assert call(state=FAKE_MIS) == gdn.GDN_EALIGN
