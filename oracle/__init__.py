@@ -151,6 +151,7 @@ def conv1d_silu_seq(x, w, conv_state, prec="f32"):
     N, T, C = x.shape
     K = w.shape[1]
     assert w.shape == (C, K) and cs.shape == (N, C, K - 1)
+    assert 1 <= K <= 65, "conv_kernel must be 1..65 (the oracle's history holds 64 taps)"
     out = np.empty_like(x)
     _lib(prec).oracle_conv1d_silu_seq(_p(x), _p(w), _p(cs), _p(out), N, T, C, K)
     return out, cs

@@ -38,6 +38,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
 #include <string.h>
 #include <stdlib.h>
 #ifdef _OPENMP
@@ -195,15 +196,23 @@ void oracle_l2norm_gqa(const real *x, real *out, long rows, int n_k_heads,
  * convolved value). A scan over T positions equals T single steps.
  *   x, out [N][T][C], w [C][K], conv_state [N][C][K-1] (updated in place)
  * ------------------------------------------------------------------------ */
+/* Longest conv history a channel may carry (the pages' widths are 2..4). */
+#define ORACLE_MAX_TAPS 64
+
 void oracle_conv1d_silu_seq(const real *x, const real *w, real *conv_state,
                             real *out, int n_seqs, int n_tokens, int conv_dim,
                             int K)
 {
     const int taps = K - 1;
+    if (K < 1 || taps > ORACLE_MAX_TAPS) {
+        fprintf(stderr, "oracle_conv1d_silu_seq: conv_kernel %d outside 1..%d\n", K,
+                ORACLE_MAX_TAPS + 1);
+        abort();
+    }
 #pragma omp parallel for collapse(2) schedule(static)
     for (int n = 0; n < n_seqs; n++) {
         for (int c = 0; c < conv_dim; c++) {
-            real hist[64];
+            real hist[ORACLE_MAX_TAPS];
             const real *wc = w + (size_t)c * K;
             real *cs = conv_state + ((size_t)n * conv_dim + c) * taps;
             for (int u = 0; u < taps; u++)
