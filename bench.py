@@ -33,8 +33,10 @@ The same line carries the other workloads of the hot path ("legs"):
               bf16 layer as one; microseconds per step of GPU time with warm
               caches (a captured HIP graph replayed) and after a 1 GiB cache
               flush, and per eager Python call (host-launch-bound)
-  machine     what this GPU achieves: a 1 GiB device copy (GB/s) and the
-              fp32 FMA-chain issue rate of gdn_probe_fma (TFLOP/s)
+  machine     what this GPU achieves: a 1 GiB device copy (GB/s), the fp32
+              FMA-chain issue rate of gdn_probe_fma (TFLOP/s), and the issue
+              rate of fp32 and bf16 matrix instructions at one wave per SIMD
+              (gdn_probe_mfma: cycles per instruction, TFLOP/s)
 and the roofline of the dominant kernel (the decode recurrence) measured with
 HIP events on the stream it runs on, and the CPU oracle timed on this host.
 
@@ -543,6 +545,17 @@ def probe_fma_fn():
     return fn
 
 
+def probe_mfma_fn():
+    """gdn_probe_mfma from the benchmark's probe library."""
+    import ctypes
+    path = os.path.join(ROOT, "linear_attention_ssm_recurrence_amd", "libgdn_probe.so")
+    fn = ctypes.CDLL(path).gdn_probe_mfma
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    return fn
+
+
 def run_machine(torch, gdn, steps):
     """What this GPU achieves: a plain device copy and the fp32 FMA issue rate."""
     src = torch.ones(256 * 1024 * 1024, device="cuda")       # 1 GiB
@@ -570,9 +583,27 @@ def run_machine(torch, gdn, steps):
         for _ in range(reps):
             fma()
     flops = blocks * 256 * iters * 32 * reps
-    return {"copy_1GiB_GBps": copy_gbps, "copy_frac_hbm_peak": copy_gbps / HBM_PEAK_GBS,
-            "fma_chain_TFLOPs": flops / (tf.event_ms * 1e-3) / 1e12,
-            "fma_chain_frac_fp32_peak": flops / (tf.event_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS}
+    res = {"copy_1GiB_GBps": copy_gbps, "copy_frac_hbm_peak": copy_gbps / HBM_PEAK_GBS,
+           "fma_chain_TFLOPs": flops / (tf.event_ms * 1e-3) / 1e12,
+           "fma_chain_frac_fp32_peak": flops / (tf.event_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS}
+    # matrix instructions at one wave per SIMD (256 workgroups of 4 waves): time per
+    # instruction per wave, in cycles at the nominal 2.4 GHz
+    mfma = probe_mfma_fn()
+    miters = 2000
+    for kind, name, fl in ((0, "f32_16x16x4", 2048), (1, "bf16_16x16x32", 16384)):
+        for chains in (1, 2, 4):
+            def run_m():
+                rc = mfma(kind, chains, out.data_ptr(), 256, miters, stream)
+                if rc != 0:
+                    raise RuntimeError(f"gdn_probe_mfma returned {rc}")
+            run_m()
+            with Timer(torch) as tm:
+                for _ in range(reps):
+                    run_m()
+            us = tm.event_ms * 1e3 / reps
+            res[f"mfma_{name}_chains{chains}_cycles"] = us * 2400.0 / (miters * chains)
+            res[f"mfma_{name}_chains{chains}_TFLOPs"] = 1024 * miters * chains * fl / (us * 1e-6) / 1e12
+    return res
 
 
 def block_layer_bytes(N, H, HK, S, K) -> int:

@@ -309,7 +309,11 @@ size_t gdn_decode_block_workspace_bytes(int n_seqs, int n_k_heads, int n_v_heads
  *              gdn_decode_block_workspace_bytes(...) bytes, 4-byte aligned,
  *              ZERO before the first call; every completed call leaves it
  *              zero again. Calls that may run at the same time (on
- *              different streams) need workspaces of their own.
+ *              different streams) need workspaces of their own. A workspace
+ *              that is not zero when a call starts (one shared by calls that
+ *              overlap, or left by a launch that did not complete) gives
+ *              wrong outputs without an error and is not cleared by later
+ *              calls: zero it again (hipMemset) before reusing it.
  *   other arguments as gdn_decode_block_bf16.
  * Errors: as gdn_decode_block_bf16; also GDN_ENULL (workspace NULL),
  * GDN_ESIZE (workspace too small), GDN_EALIGN (workspace not 4-byte aligned).

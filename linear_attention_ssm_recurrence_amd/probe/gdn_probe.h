@@ -1,9 +1,9 @@
 /*
- * gdn_probe.h: a measurement probe for the benchmark, built as its own
+ * gdn_probe.h: measurement probes for the benchmark, built as their own
  * library (libgdn_probe.so) beside libgdn.so and not part of the library's
  * interface.
  *
- * It is not a step of the Gated DeltaNet block. The benchmark calls it to
+ * They are not steps of the Gated DeltaNet block. The benchmark calls them to
  * measure what this particular MI355X achieves, so that a kernel's roofline
  * fraction can be stated against the measured figure as well as against the
  * published peak.
@@ -28,6 +28,17 @@ extern "C" {
  * rejected the launch.
  */
 int gdn_probe_fma(float *out, int n_blocks, int iters, float a, float b, void *stream);
+
+/*
+ * Matrix-instruction issue rate: n_blocks workgroups of 256 threads (four
+ * waves), each wave running `chains` independent accumulator chains of
+ * `iters` dependent matrix instructions: kind 0 v_mfma_f32_16x16x4f32 (2048
+ * flop each), kind 1 v_mfma_f32_16x16x32_bf16 (16384 flop each). With
+ * n_blocks = 256 there is one wave per SIMD. out as gdn_probe_fma.
+ * Returns 0, 1 (NULL out), 2 (bad n_blocks or iters), 3 (bad kind or chains
+ * not 1, 2 or 4), or 5 (launch rejected).
+ */
+int gdn_probe_mfma(int kind, int chains, float *out, int n_blocks, int iters, void *stream);
 
 #ifdef __cplusplus
 }

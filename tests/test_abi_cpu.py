@@ -298,6 +298,14 @@ def test_probe_is_not_in_the_library(lib):
     assert f(FAKE, 4, 0, 1.0, 0.0, NUL) == 2
     assert f(FAKE, (1 << 20) + 1, 10, 1.0, 0.0, NUL) == 2
     assert f(NUL, 4, 10, 1.0, 0.0, NUL) == 1
+    m = probe.gdn_probe_mfma
+    m.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p]
+    m.restype = ctypes.c_int
+    assert m(0, 3, FAKE, 4, 10, NUL) == 3
+    assert m(2, 1, FAKE, 4, 10, NUL) == 3
+    assert m(0, 1, NUL, 4, 10, NUL) == 1
+    assert m(1, 2, FAKE, 0, 10, NUL) == 2
 
 
 def test_ssm_a_validation(lib):
