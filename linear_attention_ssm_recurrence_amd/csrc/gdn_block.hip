@@ -139,8 +139,7 @@ __global__ __launch_bounds__(64 * kBlockWaves) void decode_block_kernel(
   if (wv < 2) {
     float* x = co + wv * S;
     const float ss = row_sumsq(x, S / 4, lane);
-    const float norm = sqrtf(ss);
-    const float inv = 1.0f / (norm > l2_eps ? norm : l2_eps);
+    const float inv = inv_l2norm(ss, l2_eps);
     for (int m = lane; m < S / 4; m += 64) {
       float4 v = load4(x + 4 * m);
       v.x = v.x * inv;
@@ -380,8 +379,7 @@ __global__ __launch_bounds__(64 * kSplitWaves) void decode_block_split_kernel(
   if (wv < 2) {
     float* x = co + wv * S;
     const float ss = row_sumsq(x, S / 4, lane);
-    const float norm = sqrtf(ss);
-    const float inv = 1.0f / (norm > l2_eps ? norm : l2_eps);
+    const float inv = inv_l2norm(ss, l2_eps);
     for (int m = lane; m < S / 4; m += 64) {
       float4 v = load4(x + 4 * m);
       v.x = v.x * inv;

@@ -35,8 +35,7 @@ __device__ __forceinline__ void l2_normalise_row(float (&x)[E], float eps) {
 #pragma unroll
   for (int e = 4; e < 8; ++e) s1 = __builtin_fmaf(x[e], x[e], s1);
   const float ss = group_sum<L>(s0) + group_sum<L>(s1);
-  const float norm = sqrtf(ss);
-  const float inv = 1.0f / (norm > eps ? norm : eps);
+  const float inv = inv_l2norm(ss, eps);
 #pragma unroll
   for (int e = 0; e < E; ++e) x[e] = x[e] * inv;
 }

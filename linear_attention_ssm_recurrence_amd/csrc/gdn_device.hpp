@@ -67,15 +67,28 @@ __device__ __forceinline__ float group_sum(float v) {
 #pragma clang fp contract(off)
 
 // SiLU in the divisor form x / (1 + e^-x) (the form both Foundry pages use),
-// with the quotient taken as x times the hardware reciprocal of 1 + e^-x
-// (v_rcp_f32, within 1 ulp) instead of a correctly rounded division, which
-// costs about ten instructions: the result is within 2 ulp of the IEEE
-// quotient, far inside the tolerance, and every kernel uses this one function,
-// so the kernels still agree with each other bit for bit. The reciprocal of
-// +inf is +0, so below x = -88 the result is still -0. e^-x itself stays
-// full precision.
+// in five instructions: e^-x as the hardware base-2 exponential of
+// -x*log2(e) (v_exp_f32), then x times the hardware reciprocal of 1 + e^-x
+// (v_rcp_f32). Rounding the product -x*log2(e) perturbs e^-x by at most
+// |x|*7e-8 relative, and each hardware instruction adds about one ulp, so the
+// result is within about 1e-7 of the exact SiLU in absolute terms and
+// (|x|*7e-8 + 4e-7) relative: far inside the tolerance, and unlike the decay's
+// exp this error does not compound (a SiLU output feeds no recurrence of its
+// own). For x below about -88, e^-x is +inf, its reciprocal +0, and the result
+// -0, as with the IEEE quotient. Every kernel uses this one function, so the
+// kernels agree with each other bit for bit.
 __device__ __forceinline__ float silu(float x) {
-  return x * __builtin_amdgcn_rcpf(1.0f + expf(-x));
+  const float e = __builtin_amdgcn_exp2f(x * -1.4426950408889634f);
+  return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// 1 / max(||x||, eps) from the sum of squares ss = ||x||^2 of an L2 norm:
+// the hardware reciprocal square root (v_rsq_f32, about one ulp) of
+// max(ss, eps^2), which has the same value up to rounding (max(sqrt(ss), eps)
+// = sqrt(max(ss, eps^2))). A NaN ss takes eps^2, as the comparison form takes
+// eps. Every L2 norm of the library uses this one function.
+__device__ __forceinline__ float inv_l2norm(float ss, float eps) {
+  return __builtin_amdgcn_rsqf(fmaxf(ss, eps * eps));
 }
 
 // Logistic sigmoid 1 / (1 + e^-x).

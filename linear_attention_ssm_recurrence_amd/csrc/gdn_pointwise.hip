@@ -60,8 +60,7 @@ __global__ __launch_bounds__(256) void l2norm_gqa_kernel(const float* __restrict
   const int d4 = head_dim >> 2;
   const float* src = x + grp * head_dim;
   const float ss = row_sumsq(src, d4, lane);
-  const float norm = sqrtf(ss);
-  const float inv = 1.0f / (norm > eps ? norm : eps);
+  const float inv = inv_l2norm(ss, eps);
   for (int m = lane; m < d4; m += 64) {
     float4 v = load4(src + 4 * m);
     v.x = v.x * inv;

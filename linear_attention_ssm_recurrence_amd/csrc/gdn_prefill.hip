@@ -85,7 +85,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_frontend_kernel(
     int part_blocks, float l2_eps) {
   constexpr int S = kPrefillS, TH = kPrefillTH, TB = kPrefillTB;
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  // the wave index is the same in every lane: held in a scalar register, it
+  // makes the head part, its kind and every address offset below that does
+  // not depend on the lane scalar as well
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, li = lane & 31;
   const int n_parts = 2 * n_k_heads + n_v_heads;
   const int pblk = blockIdx.x % part_blocks;
@@ -153,10 +156,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_frontend_kernel(
   // every input of the half-wave's positions, loaded before any arithmetic
   // (positions past the end read the last one and are zeroed at use)
   uint2 xbits[TH];
+  const uint16_t* xrow = xn + (int64_t)tb * C + c;
+  const uint16_t* xlast = xn + (int64_t)(n_tokens - 1) * C + c;
 #pragma unroll
   for (int s = 0; s < TH; ++s) {
-    const int t = tb + s < n_tokens ? tb + s : n_tokens - 1;
-    xbits[s] = *reinterpret_cast<const uint2*>(xn + (int64_t)t * C + c);
+    const uint16_t* p = tb + s < n_tokens ? xrow + (int64_t)s * C : xlast;
+    xbits[s] = *reinterpret_cast<const uint2*>(p);
   }
   // the decay gate and beta inputs of the wave's positions (v parts)
   const bool gate_lane = (kind == 2 && lane < TB && t0 + lane < n_tokens);
@@ -169,7 +174,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_frontend_kernel(
     gsa = ssm_a[head];
   }
 
-  const int64_t HKS = (int64_t)n_k_heads * S, HS = (int64_t)n_v_heads * S;
+  // this lane's output row at its half-wave's first position; one position
+  // further is one row of the q/k (HK*S) or v (H*S) output further
+  const int64_t ostride = kind < 2 ? (int64_t)n_k_heads * S : (int64_t)n_v_heads * S;
+  float* obase = (kind == 0 ? qo : kind == 1 ? ko : vo) + (int64_t)head * S +
+                 (n * (int64_t)n_tokens + t0) * ostride;
+  float* orow = obase + (int64_t)(half * TH) * ostride + 4 * li;
 #pragma unroll
   for (int s = 0; s < TH; ++s) {  // the same trip count in every lane: reductions stay whole
     const int t = tb + s;
@@ -188,7 +198,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_frontend_kernel(
       for (int u = 0; u + 1 < K - 1; ++u) hist[j][u] = hist[j][u + 1];
       hist[j][K - 2] = xv[j];
     }
-    const int64_t tok = n * (int64_t)n_tokens + t;
+    float* dst = orow + (int64_t)s * ostride;
     if (kind < 2) {
 #pragma clang fp contract(off)
       float ss = 0.0f;
@@ -197,14 +207,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_frontend_kernel(
       ss = __builtin_fmaf(o[2], o[2], ss);
       ss = __builtin_fmaf(o[3], o[3], ss);
       ss = group_sum<32>(ss);
-      const float norm = sqrtf(ss);
-      const float inv = 1.0f / (norm > l2_eps ? norm : l2_eps);
-      if (valid) {
-        float* dst = (kind == 0 ? qo : ko) + tok * HKS + (int64_t)head * S + 4 * li;
-        store4(dst, make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv));
-      }
+      const float inv = inv_l2norm(ss, l2_eps);
+      if (valid) store4(dst, make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv));
     } else if (valid) {
-      store4(vo + tok * HS + (int64_t)head * S + 4 * li, make_float4(o[0], o[1], o[2], o[3]));
+      store4(dst, make_float4(o[0], o[1], o[2], o[3]));
     }
   }
   if (owner) {
