@@ -131,3 +131,54 @@ def test_noalloc_at_capacity():
             torch.zeros((N1, C, K - 1), device=DEV), torch.zeros((N1, H, S, S), device=DEV),
             torch.zeros((N1, H, S), device=DEV), HK, 0.1)
     assert e.value.code == gdn.GDN_ESIZE
+
+
+def test_noalloc_captured_graph_replays():
+    """The allocation-free layer captured in a HIP graph (the callers it is
+    for include code under capture), replayed four times with eager work and
+    synchronisation between the replays: every replay equals eager calls of
+    the workspace form, bit for bit, chained on the same buffers."""
+    print("noalloc: graph capture", flush=True)
+    rng = np.random.default_rng(740)
+    d = _rand_layer(rng, 6, 16, 2, 4)
+    N, H, S = d["z"].shape
+    HK = 16
+    scale = 1.0 / math.sqrt(S)
+    fixed = [dev(d["conv_w"]), dev_ssm_a(d["A_log"]), dev(d["dt_bias"]), dev(d["norm_w"])]
+    act = [dev_bits(d["qkv"]), dev_bits(d["z"]), dev(d["a"]), dev(d["b"])]
+
+    def bufs():
+        return {"cs": dev(d["conv_state"]), "st": dev(d["state"]),
+                "out": torch.empty((N, H, S), dtype=torch.float32, device=DEV)}
+
+    ws = torch.zeros(gdn.gdn_decode_block_workspace_bytes(N, HK, H), dtype=torch.uint8,
+                     device=DEV)
+    eager, ref = bufs(), []
+    for _ in range(4):
+        gdn.gdn_decode_block_bf16_ex(*act, *fixed, eager["cs"], eager["st"], eager["out"], ws,
+                                     HK, scale, 1e-6, 1e-6)
+        torch.cuda.synchronize()
+        ref.append({k: v.clone() for k, v in eager.items()})
+
+    cap = bufs()
+    warm = bufs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):           # a first call outside the capture
+        gdn.gdn_decode_block_bf16_noalloc(*act, *fixed, warm["cs"], warm["st"], warm["out"], HK,
+                                          scale, 1e-6, 1e-6)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gdn.gdn_decode_block_bf16_noalloc(*act, *fixed, cap["cs"], cap["st"], cap["out"], HK,
+                                          scale, 1e-6, 1e-6)
+    torch.cuda.synchronize()
+    for r in range(4):
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in ("out", "st", "cs"):
+            assert torch.equal(cap[k], ref[r][k]), f"replay {r}: {k} differs from eager"
+        scratch = torch.randn(1 << 20, device=DEV)    # eager work between replays
+        scratch.mul_(2.0)
+        torch.cuda.synchronize()
