@@ -196,6 +196,47 @@ def test_conv_4096x8192_full():
     assert np.array_equal(host(cs), cs_ref), "conv 4096x8192 history"
 
 
+def _misaligned(a):
+    """a on the device at a 4-byte (not 16-byte) aligned address."""
+    buf = torch.empty(a.size + 1, dtype=torch.float32, device=DEV)
+    v = buf[1:].view(a.shape)
+    v.copy_(torch.from_numpy(np.ascontiguousarray(a)))
+    return v
+
+
+@pytest.mark.parametrize("K", [2, 3, 4])
+@pytest.mark.parametrize("N,T,C", [(3, 1, 4), (2, 19, 1028), (1, 45, 64), (2, 8, 2048)])
+def test_conv_four_channel_and_scalar_paths(K, N, T, C):
+    """C a multiple of 4: with 16-byte aligned buffers the scan takes four
+    channels per thread, with a misaligned one the per-channel scan. Outputs,
+    history and snapshots of both bit for bit, and against the oracle; T
+    spans chunk boundaries with a ragged last chunk, C = 1028 a ragged last
+    channel block."""
+    rng = np.random.default_rng(3100 + 100 * K + T + C)
+    x = rng.standard_normal((N, T, C)).astype(np.float32)
+    w = (rng.standard_normal((C, K)) * 0.5).astype(np.float32)
+    cs0 = rng.standard_normal((N, C, K - 1)).astype(np.float32)
+    out_ref, cs_ref = oracle.conv1d_silu_seq(x, w, cs0)
+    res = []
+    for place in (dev, _misaligned):
+        cs = place(cs0)
+        out = place(np.full((N, T, C), np.nan, dtype=np.float32))
+        snaps = place(np.full((N, T, C, K - 1), np.nan, dtype=np.float32))
+        assert (cs.data_ptr() % 16 == 0) == (place is dev)
+        gdn.gdn_conv1d_silu_seq_ex(place(x), place(w), cs, out, snaps)
+        res.append((out, cs, snaps))
+    torch.cuda.synchronize()
+    for a, b, nm in zip(res[0], res[1], ("out", "history", "snaps")):
+        assert torch.equal(a, b), f"conv K={K} C={C}: four-channel {nm} != per-channel {nm}"
+    out, cs, snaps = res[0]
+    assert_close(host(out), out_ref, f"conv K={K} T={T} C={C} out")
+    assert np.array_equal(host(cs), cs_ref), f"conv K={K} T={T} C={C} history"
+    hist = np.concatenate([cs0, x.transpose(0, 2, 1)], axis=2)   # [N][C][K-1+T]
+    sn = host(snaps)
+    for t in range(T):
+        assert np.array_equal(sn[:, t], hist[:, :, t + 1:t + K]), f"conv snapshot {t}"
+
+
 # ---------------------------------------------------------------------------
 # Companions
 # ---------------------------------------------------------------------------
