@@ -22,10 +22,11 @@
 namespace gdn {
 
 // Positions per thread of the four-channel scan. Measured at 1 x 4096 x 8192
-// (K = 4), one launch each: 4 positions with non-temporal output stores
-// 41.0 us, 8 positions 41.6 us, 8 positions with ordinary stores 43.0 us; the
-// per-channel scan 44.0 us.
-constexpr int kConvTB4 = 4;
+// (K = 4) with the input cold (four input/output sets in rotation, 1 GiB,
+// beyond the last-level cache): 8 positions 45.3 us per launch, 12 45.6,
+// 16 49.0, 4 53.5; the per-channel scan 51.4 us with ordinary access and
+// 46.8 us with non-temporal access.
+constexpr int kConvTB4 = 8;
 
 template <int K>
 __global__ __launch_bounds__(256) void conv_step_kernel(const float* __restrict__ x,
@@ -94,17 +95,19 @@ __global__ __launch_bounds__(256) void conv_scan_kernel(const float* __restrict_
     }
   }
   // every input of the chunk loaded before any arithmetic, so the loads are
-  // in flight together (positions past the end read the last one, unused)
+  // in flight together (positions past the end read the last one, unused);
+  // inputs and outputs are touched once per launch: non-temporal
   float xs[TB];
 #pragma unroll
   for (int i = 0; i < TB; ++i) {
     const int t = t0 + i < n_tokens ? t0 + i : n_tokens - 1;
-    xs[i] = xc[(int64_t)t * conv_dim];
+    xs[i] = __builtin_nontemporal_load(xc + (int64_t)t * conv_dim);
   }
 #pragma unroll
   for (int i = 0; i < TB; ++i) {
     const int t = t0 + i;
-    if (t < n_tokens) oc[(int64_t)t * conv_dim] = conv_point<K>(xs[i], hist, wc);
+    if (t < n_tokens)
+      __builtin_nontemporal_store(conv_point<K>(xs[i], hist, wc), oc + (int64_t)t * conv_dim);
 #pragma unroll
     for (int u = 0; u + 1 < K - 1; ++u) hist[u] = hist[u + 1];
     hist[K - 2] = xs[i];
@@ -199,7 +202,10 @@ __global__ __launch_bounds__(256) void conv_scan4_kernel(const float* __restrict
 #pragma unroll
   for (int i = 0; i < TB; ++i) {
     const int t = t0 + i < n_tokens ? t0 + i : n_tokens - 1;
-    xs[i] = load4(xc + (int64_t)t * conv_dim);
+    // non-temporal except the last K-1 positions, which the next chunk's
+    // thread reads again as its halo
+    xs[i] = (i >= TB - H1) ? load4(xc + (int64_t)t * conv_dim)
+                           : load4_stream(xc + (int64_t)t * conv_dim);
   }
 #pragma unroll
   for (int i = 0; i < TB; ++i) {
