@@ -133,9 +133,9 @@ int gdn_conv1d_silu(const float *x, const float *w, float *conv_state, float *ou
  * fmssm_conv1d_silu_seq; [CU] fc_ssm_conv1d_silu_seq). Every position's
  * output and the final conv_state equal n_tokens single steps bit for bit.
  *   x, out [n_seqs][n_tokens][conv_dim]
- * Any 4-byte alignment is accepted; with conv_dim a multiple of 4 and every
- * buffer 16-byte aligned the scan moves four channels per vector access
- * (same bits, fewer memory instructions).
+ * Any 4-byte alignment is accepted; with conv_dim a multiple of 4, every
+ * buffer 16-byte aligned and n_tokens > 8 the scan moves four channels per
+ * vector access (same bits, fewer memory instructions).
  * Other arguments and errors as gdn_conv1d_silu.
  */
 int gdn_conv1d_silu_seq(const float *x, const float *w, float *conv_state, float *out,

@@ -11,8 +11,9 @@
 // The history is nothing but the last K-1 raw inputs, so no output depends on
 // an earlier output: the scan is data-parallel over positions as well as over
 // channels. Each thread takes one channel (four consecutive channels when
-// conv_dim is a multiple of 4 and the buffers are 16-byte aligned, so that
-// every access is a 16-byte vector) and a chunk of positions, reading K-1
+// conv_dim is a multiple of 4, the buffers are 16-byte aligned and there are
+// more than 8 positions, so that every access is a 16-byte vector) and a
+// chunk of positions, reading K-1
 // inputs before its chunk as a halo (from conv_state for positions before
 // the first). Every kernel evaluates each position with the same conv_point,
 // so the scans and single steps agree bit for bit.
@@ -271,8 +272,12 @@ static int launch_conv_step(const float* x, const float* w, float* cs, float* ou
 template <int K>
 static int launch_conv_scan(const float* x, const float* w, float* cs, float* out, float* snaps,
                             int n_seqs, int n_tokens, int conv_dim, hipStream_t s) {
-  if (conv_dim % 4 == 0 && aligned16(x) && aligned16(w) && aligned16(cs) && aligned16(out) &&
-      (!snaps || aligned16(snaps))) {
+  // With one chunk of positions or fewer (a speculative verify of a few
+  // tokens) the four-channel scan would run a quarter of the threads in a
+  // single round of waves: the per-channel scan hides the memory latency
+  // better there (measured at 64 x 4 x 8192 with snapshots).
+  if (n_tokens > kConvTB4 && conv_dim % 4 == 0 && aligned16(x) && aligned16(w) &&
+      aligned16(cs) && aligned16(out) && (!snaps || aligned16(snaps))) {
     constexpr int TB4 = kConvTB4;
     const int c_blocks = (conv_dim / 4 + 255) / 256;
     const int t_chunks = (n_tokens + TB4 - 1) / TB4;

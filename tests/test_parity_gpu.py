@@ -205,13 +205,15 @@ def _misaligned(a):
 
 
 @pytest.mark.parametrize("K", [2, 3, 4])
-@pytest.mark.parametrize("N,T,C", [(3, 1, 4), (2, 19, 1028), (1, 45, 64), (2, 8, 2048)])
+@pytest.mark.parametrize("N,T,C", [(3, 1, 4), (2, 19, 1028), (1, 45, 64), (2, 8, 2048),
+                                   (1, 9, 8)])
 def test_conv_four_channel_and_scalar_paths(K, N, T, C):
-    """C a multiple of 4: with 16-byte aligned buffers the scan takes four
-    channels per thread, with a misaligned one the per-channel scan. Outputs,
-    history and snapshots of both bit for bit, and against the oracle; T
-    spans chunk boundaries with a ragged last chunk, C = 1028 a ragged last
-    channel block."""
+    """C a multiple of 4: with 16-byte aligned buffers and more than 8
+    positions the scan takes four channels per thread, with a misaligned
+    buffer (or T <= 8) the per-channel scan. Outputs, history and snapshots
+    of both bit for bit, and against the oracle; T spans chunk boundaries
+    with a ragged last chunk (T = 9: one position in the second), C = 1028 a
+    ragged last channel block."""
     rng = np.random.default_rng(3100 + 100 * K + T + C)
     x = rng.standard_normal((N, T, C)).astype(np.float32)
     w = (rng.standard_normal((C, K)) * 0.5).astype(np.float32)
