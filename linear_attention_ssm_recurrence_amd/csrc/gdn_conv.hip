@@ -13,10 +13,10 @@
 // channels. Each thread takes one channel (four consecutive channels when
 // conv_dim is a multiple of 4, the buffers are 16-byte aligned and there are
 // more than 8 positions, so that every access is a 16-byte vector) and a
-// chunk of positions, reading K-1
-// inputs before its chunk as a halo (from conv_state for positions before
-// the first). Every kernel evaluates each position with the same conv_point,
-// so the scans and single steps agree bit for bit.
+// chunk of positions, reading K-1 inputs before its chunk as a halo (from
+// conv_state for positions before the first). Every kernel evaluates each
+// position with the same conv_point, so the scans and single steps agree bit
+// for bit.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -24,9 +24,9 @@ namespace gdn {
 
 // Positions per thread of the four-channel scan. Measured at 1 x 4096 x 8192
 // (K = 4) with the input cold (four input/output sets in rotation, 1 GiB,
-// beyond the last-level cache): 8 positions 45.3 us per launch, 12 45.6,
-// 16 49.0, 4 53.5; the per-channel scan 51.4 us with ordinary access and
-// 46.8 us with non-temporal access.
+// beyond the last-level cache): 8 positions 44.4-45.3 us per launch, 12
+// 45.6, 16 49.0, 4 53.5; the per-channel scan 49.4-51.4 us with ordinary
+// access and 46.2-46.8 us with non-temporal access.
 constexpr int kConvTB4 = 8;
 
 template <int K>
@@ -127,7 +127,8 @@ __global__ __launch_bounds__(256) void conv_scan_kernel(const float* __restrict_
 }
 
 // The same scan with four consecutive channels per thread (conv_dim a
-// multiple of 4, every pointer 16-byte aligned): each input and output row
+// multiple of 4, every pointer 16-byte aligned, more than TB positions, so
+// that a sequence spans at least two chunks): each input and output row
 // piece is one float4, and a channel group's weights, history and history
 // snapshots (4 (K-1) or 4 K consecutive floats) are whole float4s. Each
 // channel goes through the same conv_point in the same order as in
